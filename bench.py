@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  causal forward + backward on the 1024-token workload (B=4, H=8, T=1024,
+  d=64, fp32), then one batched paged decode (32 sequences, Hq=16, Hkv=4,
+  d=64, 16-token pages, context lengths uniform in [512, 4096]).
+All inputs are generated once and already resident in HBM when timing starts.
+
+Printed: one JSON line.  `value` is the causal forward+backward rate in
+algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
+QK^T recompute, dV, dP, dK, dQ backward) over the summed event times of the two
+calls; the decode rate (algorithmic HBM bytes per call / call time) and the
+8192-token grouped-query forward are reported beside it.  Each decode call
+reads a different one of several pool replicas so the 256 MB last-level cache
+cannot serve a repeated pool.
+
+`roofline` describes the dominant kernel (the backward: its delta/zero-fill
+pass plus the main KV-parallel kernel, launched together by attn_causal_bwd),
+measured with HIP events on the launch stream.  `cpu_baseline` is the CPU
+oracle (plain double-precision materialised attention) timed on this host on
+the full 1024-token forward+backward.
+"""
+import argparse
+import json
+import math
+import os
+import platform
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s (fp32, % MFMA peak); paged-decode HBM GB/s"
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+CAUSAL = "mha_b4_h8_t1024_d64"
+GQA = "gqa_b1_hq16_hkv4_t8192_d64"
+DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
+
+
+def causal_flops(B, Hq, T, D):
+    pairs = B * Hq * T * (T + 1) // 2
+    return 4 * D * pairs, 10 * D * pairs
+
+
+def decode_bytes(d, Hq, Hkv, D):
+    ctx = [int(c) for c in d["context_lens"]]
+    S = len(ctx)
+    pages = sum(math.ceil(c / d["page_size"]) for c in ctx)
+    kv = sum(ctx) * Hkv * D * 4 * 2          # every K and V row once per KV head
+    qo = 2 * S * Hq * D * 4                  # q in, o out
+    return kv + qo + S * Hq * 4 + pages * 4 + S * 4  # + lse, used table entries, lengths
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-replicas", type=int, default=4)
+    ap.add_argument("--gqa-iters", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-runs", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_self_attention_amd as attn
+    import synthetic_inputs as si
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- inputs and outputs, resident before timing ----
+    cfg = si.CAUSAL_WORKLOADS[CAUSAL]
+    B, Hq, Hkv, T, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["D"]
+    host = si.causal_workload(CAUSAL)
+    x = {k: v.to(dev) for k, v in host.items()}
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, Hq, T), device=dev)
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    ws = torch.empty((attn.attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D) // 4,), device=dev)
+    fwd_flops, bwd_flops = causal_flops(B, Hq, T, D)
+
+    dcfg = si.DECODE_WORKLOADS[DECODE]
+    dh = si.decode_workload(DECODE)
+    dq_ = dh["q"].to(dev)
+    bt = dh["block_table"].to(dev)
+    ctx = dh["context_lens"].to(dev)
+    pools = []
+    for r in range(max(1, args.decode_replicas)):
+        pools.append((dh["k_pool"].to(dev), dh["v_pool"].to(dev)))
+    do_ = torch.empty_like(dq_)
+    dlse = torch.empty((dcfg["S"], dcfg["Hq"]), device=dev)
+    dws = torch.empty((attn.attn_paged_decode_workspace_bytes(dcfg["S"], dcfg["Hq"], dcfg["Hkv"], dcfg["D"],
+                                                              dcfg["page_size"], dcfg["max_pages"]) // 4,),
+                      device=dev)
+    dbytes = decode_bytes(dh, dcfg["Hq"], dcfg["Hkv"], dcfg["D"])
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        attn.attn_causal_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        attn.attn_causal_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq=dq, dk=dk, dv=dv, workspace=ws,
+                             stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        kp, vp = pools[i % len(pools)]
+        attn.attn_paged_decode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
+    t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
+    t_dec = [e[2].elapsed_time(e[3]) for e in evs]
+    t_step = [e[0].elapsed_time(e[3]) for e in evs]
+    sum_fwd, sum_bwd = sum(t_fwd), sum(t_bwd)
+    K = args.steps
+
+    # headline: fwd+bwd algorithmic TFLOP/s over the summed event time of the two calls
+    value = (fwd_flops + bwd_flops) * K / ((sum_fwd + sum_bwd) * 1e-3) / 1e12
+    bwd_avg_s = sum_bwd / K * 1e-3
+    bwd_tflops = bwd_flops / bwd_avg_s / 1e12
+    fwd_avg_s = sum_fwd / K * 1e-3
+    dec_avg_s = sum(t_dec) / K * 1e-3
+    dec_gbps = dbytes / dec_avg_s / 1e9
+
+    # the 8192-token grouped-query forward (O + LSE), timed separately
+    gcfg = si.CAUSAL_WORKLOADS[GQA]
+    gh = si.causal_workload(GQA)
+    gx = {k: v.to(dev) for k, v in gh.items()}
+    go = torch.empty_like(gx["q"])
+    glse = torch.empty((gcfg["B"], gcfg["Hq"], gcfg["T"]), device=dev)
+    attn.attn_causal_fwd(gx["q"], gx["k"], gx["v"], o=go, lse=glse, stream=stream)
+    torch.cuda.synchronize()
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.gqa_iters)]
+    for a, b in gev:
+        a.record(stream)
+        attn.attn_causal_fwd(gx["q"], gx["k"], gx["v"], o=go, lse=glse, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    g_ms = statistics.median(a.elapsed_time(b) for a, b in gev)
+    g_flops, _ = causal_flops(gcfg["B"], gcfg["Hq"], gcfg["T"], gcfg["D"])
+    del gx, go, glse
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(sum(t_step) / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{CAUSAL} causal fwd+bwd + {DECODE} paged decode (one step)",
+            "causal": {"B": B, "Hq": Hq, "Hkv": Hkv, "T": T, "D": D, "scale": 1 / math.sqrt(D)},
+            "decode": {k: dcfg[k] for k in ("S", "Hq", "Hkv", "D", "page_size", "ctx_lo", "ctx_hi", "max_pages")},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "attn_causal_bwd (attn_bwd_pre + attn_bwd_main)",
+            "bound": "mfma",
+            "achieved": round(bwd_tflops, 3),
+            "peak": PEAK_FP32_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": bwd_flops,
+            "avg_launch_us": round(bwd_avg_s * 1e6, 2),
+        },
+        "fwd_bwd": {
+            "fwd_us": round(fwd_avg_s * 1e6, 2), "bwd_us": round(bwd_avg_s * 1e6, 2),
+            "fwd_tflops": round(fwd_flops / fwd_avg_s / 1e12, 3), "bwd_tflops": round(bwd_tflops, 3),
+            "fwd_bwd_tflops": round(value, 3), "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
+            "fwd_us_median": round(statistics.median(t_fwd) * 1e3, 2),
+            "bwd_us_median": round(statistics.median(t_bwd) * 1e3, 2),
+        },
+        "decode": {
+            "us": round(dec_avg_s * 1e6, 2), "us_median": round(statistics.median(t_dec) * 1e3, 2),
+            "bytes_per_call": dbytes, "gbps": round(dec_gbps, 1),
+            "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4), "pool_replicas": len(pools),
+        },
+        "gqa_t8192_fwd": {
+            "ms_median": round(g_ms, 4), "tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 3),
+            "frac_of_fp32_mfma_peak": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    if not args.no_cpu_baseline:
+        from oracle import oracle as oracle_mod
+        orc = oracle_mod.default()
+        runs = []
+        for _ in range(max(1, args.cpu_runs)):
+            t = time.perf_counter()
+            orc.causal_fwd(host["q"], host["k"], host["v"])
+            orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+            runs.append(time.perf_counter() - t)
+        cpu_s = statistics.median(runs)
+        line["cpu_baseline"] = {
+            "value": round((fwd_flops + bwd_flops) / cpu_s / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"full {CAUSAL} forward+backward (materialised, double), median of {len(runs)} runs, "
+                      f"{cpu_s:.2f} s each; host {cpu_model()}",
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""MI355X (gfx950) causal attention: flash-style forward, its VJP and paged decode.
+
+The computation runs in the HIP kernels of ``libattn.so`` behind a C ABI
+(``include/attn.h``); this package is a thin ctypes binding with the same
+names.  torch is used only for device memory and streams.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_ABI_VERSION,
+    ATTN_DEVICE_ERROR,
+    ATTN_INVALID_ARGUMENT,
+    ATTN_OK,
+    ATTN_UNSUPPORTED,
+    ATTN_WORKSPACE_TOO_SMALL,
+    AttnError,
+    attn_abi_version,
+    attn_causal_bwd,
+    attn_causal_bwd_workspace_bytes,
+    attn_causal_fwd,
+    attn_last_error,
+    attn_paged_decode,
+    attn_paged_decode_workspace_bytes,
+    lib,
+    library_path,
+)

@@ -1,0 +1,242 @@
+// C ABI of the attention library: argument validation, error reporting and
+// dispatch to the gfx950 kernels.
+//
+// Conventions ("Execution Backends and the Python ABI", "Stable C ABI"): status
+// returns, thread-local error details, every exception caught at the boundary,
+// no C++ type in the signatures.  Shapes are checked before anything else runs
+// ("Architecture", "Tensor conventions": incompatible shapes fail immediately),
+// and all checks finish before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+attn_status ok() {
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+struct Range {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+    const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output range must be disjoint from every input and every other output.
+attn_status check_disjoint(std::initializer_list<Range> outs, std::initializer_list<Range> ins) {
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Range& i : ins)
+            if (overlaps(*o, i))
+                return fail(ATTN_INVALID_ARGUMENT,
+                            std::string("output '") + o->name + "' overlaps input '" + i.name + "'");
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlaps(*o, *o2))
+                return fail(ATTN_INVALID_ARGUMENT,
+                            std::string("outputs '") + o->name + "' and '" + o2->name + "' overlap");
+    }
+    return ATTN_OK;
+}
+
+attn_status check_ptr(const void* p, const char* name, size_t align) {
+    if (!p) return fail(ATTN_INVALID_ARGUMENT, std::string("'") + name + "' is NULL");
+    if ((uintptr_t)p % align != 0)
+        return fail(ATTN_INVALID_ARGUMENT,
+                    std::string("'") + name + "' is not " + std::to_string(align) + "-byte aligned");
+    return ATTN_OK;
+}
+
+#define ATTN_TRY(expr)                         \
+    do {                                       \
+        attn_status st_ = (expr);              \
+        if (st_ != ATTN_OK) return st_;        \
+    } while (0)
+
+const int64_t kMaxElems = (int64_t)1 << 31;  // per-head T*D and index arithmetic limit
+
+// Shape checks shared by the two causal calls.
+attn_status check_causal_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0)
+        return fail(ATTN_INVALID_ARGUMENT, "B, Hq, Hkv, T and D must all be positive (got B=" + std::to_string(B) +
+                                               " Hq=" + std::to_string(Hq) + " Hkv=" + std::to_string(Hkv) +
+                                               " T=" + std::to_string(T) + " D=" + std::to_string(D) + ")");
+    if (Hq % Hkv != 0)
+        return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads (Hq=" +
+                                               std::to_string(Hq) + ", Hkv=" + std::to_string(Hkv) + ")");
+    if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
+    if (T * D >= kMaxElems || B * Hq >= kMaxElems || T >= kMaxElems / 64)
+        return fail(ATTN_INVALID_ARGUMENT, "tensor too large: T*D and B*Hq must stay below 2^31");
+    if (!attn::causal_head_dim_supported(D))
+        return fail(ATTN_UNSUPPORTED, "head width D=" + std::to_string(D) +
+                                          " has no kernel (supported: 8, 16, 32, 64, 128)");
+    return ATTN_OK;
+}
+
+attn_status device_ready() {
+    int n = 0;
+    hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0)
+        return fail(ATTN_DEVICE_ERROR, std::string("no HIP device: ") +
+                                           (e != hipSuccess ? hipGetErrorString(e) : "device count is 0"));
+    int dev = -1;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_DEVICE_ERROR, std::string("no current HIP device: ") + hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+attn_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ATTN_DEVICE_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+namespace attn {
+bool causal_head_dim_supported(int64_t D) { return D == 8 || D == 16 || D == 32 || D == 64 || D == 128; }
+}  // namespace attn
+
+extern "C" {
+
+uint32_t attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status attn_causal_fwd(const float* q, const float* k, const float* v, int64_t B, int64_t Hq, int64_t Hkv,
+                            int64_t T, int64_t D, float scale, float* o, float* lse, void* stream) {
+    try {
+        ATTN_TRY(check_causal_shape(B, Hq, Hkv, T, D, scale));
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k, "k", 16));
+        ATTN_TRY(check_ptr(v, "v", 16));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        ATTN_TRY(check_ptr(lse, "lse", 4));
+        const size_t qb = (size_t)(B * Hq * T * D) * 4, kb = (size_t)(B * Hkv * T * D) * 4;
+        const size_t lb = (size_t)(B * Hq * T) * 4;
+        ATTN_TRY(check_disjoint({{o, qb, "o"}, {lse, lb, "lse"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+        ATTN_TRY(device_ready());
+        attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, T, D, scale};
+        return launched(attn::launch_causal_fwd(a, (hipStream_t)stream), "attn_causal_fwd launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_causal_fwd: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_causal_fwd: unknown exception");
+    }
+}
+
+size_t attn_causal_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
+    if (T * D >= kMaxElems || B * Hq >= kMaxElems) return 0;
+    const size_t bytes = attn::bwd_workspace_floats(B, Hq, T) * 4;
+    return (bytes + 255) / 256 * 256;
+}
+
+attn_status attn_causal_bwd(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                            const float* dout, int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale,
+                            float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        ATTN_TRY(check_causal_shape(B, Hq, Hkv, T, D, scale));
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k, "k", 16));
+        ATTN_TRY(check_ptr(v, "v", 16));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        ATTN_TRY(check_ptr(lse, "lse", 4));
+        ATTN_TRY(check_ptr(dout, "dout", 16));
+        ATTN_TRY(check_ptr(dq, "dq", 16));
+        ATTN_TRY(check_ptr(dk, "dk", 16));
+        ATTN_TRY(check_ptr(dv, "dv", 16));
+        ATTN_TRY(check_ptr(workspace, "workspace", 16));
+        const size_t need = attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D);
+        if (workspace_bytes < need)
+            return fail(ATTN_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) +
+                                                      " bytes, attn_causal_bwd needs " + std::to_string(need));
+        const size_t qb = (size_t)(B * Hq * T * D) * 4, kb = (size_t)(B * Hkv * T * D) * 4;
+        const size_t lb = (size_t)(B * Hq * T) * 4;
+        ATTN_TRY(check_disjoint({{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"}},
+                                {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {lse, lb, "lse"},
+                                 {dout, qb, "dout"}}));
+        ATTN_TRY(device_ready());
+        attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, Hq, Hkv, T, D, scale};
+        return launched(attn::launch_causal_bwd(a, (hipStream_t)stream), "attn_causal_bwd launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_causal_bwd: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_causal_bwd: unknown exception");
+    }
+}
+
+size_t attn_paged_decode_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                                         int64_t max_pages_per_seq) {
+    if (S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 || Hq % Hkv != 0)
+        return 0;
+    if (page_size * max_pages_per_seq >= kMaxElems || S * Hq >= kMaxElems) return 0;
+    const size_t bytes = attn::decode_workspace_floats(S, Hq, Hkv, D, page_size, max_pages_per_seq) * 4;
+    return (bytes + 255) / 256 * 256;
+}
+
+attn_status attn_paged_decode(const float* q, const float* k_pool, const float* v_pool, const int32_t* block_table,
+                              const int32_t* context_lens, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                              int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages, float scale, float* o,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        if (S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+            return fail(ATTN_INVALID_ARGUMENT,
+                        "S, Hq, Hkv, D, page_size, max_pages_per_seq and num_pages must all be positive");
+        if (Hq % Hkv != 0)
+            return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads");
+        if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
+        if (page_size * max_pages_per_seq >= kMaxElems || S * Hq >= kMaxElems ||
+            num_pages * Hkv * page_size * D >= ((int64_t)1 << 40))
+            return fail(ATTN_INVALID_ARGUMENT, "sizes too large: page_size*max_pages_per_seq must stay below 2^31");
+        if (!attn::decode_shape_supported(D, page_size, Hq / Hkv))
+            return fail(ATTN_UNSUPPORTED, "no decode kernel for D=" + std::to_string(D) + ", page_size=" +
+                                              std::to_string(page_size) + ", Hq/Hkv=" + std::to_string(Hq / Hkv) +
+                                              " (supported: D in {8,16,32,64,128}, page_size in {16,32,64}, "
+                                              "Hq/Hkv in {1,2,4,8} with Hq/Hkv*D <= 512)");
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
+        ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
+        ATTN_TRY(check_ptr(block_table, "block_table", 4));
+        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        if (lse) ATTN_TRY(check_ptr(lse, "lse", 4));
+        ATTN_TRY(check_ptr(workspace, "workspace", 16));
+        const size_t need = attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages_per_seq);
+        if (workspace_bytes < need)
+            return fail(ATTN_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) +
+                                                      " bytes, attn_paged_decode needs " + std::to_string(need));
+        const size_t qb = (size_t)(S * Hq * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
+        const size_t tb = (size_t)(S * max_pages_per_seq) * 4, cb = (size_t)S * 4, lb = (size_t)(S * Hq) * 4;
+        const Range lr{lse, lse ? lb : 0, "lse"};
+        ATTN_TRY(check_disjoint({{o, qb, "o"}, lr, {workspace, need, "workspace"}},
+                                {{q, qb, "q"}, {k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
+                                 {block_table, tb, "block_table"}, {context_lens, cb, "context_lens"}}));
+        ATTN_TRY(device_ready());
+        attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, (float*)workspace,
+                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale};
+        return launched(attn::launch_paged_decode(a, (hipStream_t)stream), "attn_paged_decode launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_decode: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_paged_decode: unknown exception");
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,334 @@
+// Causal attention backward on gfx950: the vector-Jacobian product (dQ, dK, dV)
+// of the forward for the loss sum(dO * O), recomputing the probabilities from
+// Q, K and the saved per-row log-sum-exp.
+//
+// What is computed: "Execution Backends and the Python ABI", "What the Metal
+// slice does" (the Flash backward recomputes scores and probabilities from Q, K
+// and the row statistics and never allocates a quadratic buffer); "Architecture",
+// "Tensor conventions" (the mask).  Gradients of a key/value head that several
+// query heads share are summed over those heads (learn/neural_network page,
+// "Layer normalization": a broadcast input's gradient is reduced back to its own
+// shape).  With P = exp(s - LSE), dP = dO V^T, Delta_i = <dO_i, O_i> and
+// dS = P (dP - Delta):  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Kernels, in stream order:
+//   1. attn_bwd_pre: Delta_i = <dO_i, O_i> into the workspace, and dQ = 0;
+//   2. attn_bwd_main: one work-group per 64-key block of one (batch, KV head);
+//      wave w owns keys kv0+16w .. +15 and keeps their K, V fragments and dK, dV
+//      accumulators in registers while it walks every query tile at or below
+//      the diagonal, for each query head of the group.  Per query tile (64 rows,
+//      Q and dO staged in LDS):
+//        S  = Q K^T, dP = dO V^T           (C tiles: key in the lane i)
+//        P, dS                             (elementwise, masked on the diagonal)
+//        dV^T += dO^T P,  dK^T += Q^T dS   (P and dS are the B operands as-is)
+//        dS -> LDS, then dQ(16 rows per wave) = dS K, added to dQ with float
+//        atomics (the contraction runs over the whole 64-key block).
+#include "attn_launch.h"
+#include "device_common.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------------------
+// 1. Delta = rowsum(dO * O), dQ = 0
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const float* __restrict__ O,
+                                                           const float* __restrict__ dO,
+                                                           float* __restrict__ Delta,
+                                                           float* __restrict__ dQ, int64_t rows) {
+    constexpr int TPR = D / 4;  // threads per row, one float4 each
+    constexpr int RPB = 256 / TPR;
+    const int tid = threadIdx.x;
+    const int part = tid % TPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+    float x = 0.f;
+    if (row < rows) {
+        const f32x4 o = *(const f32x4*)(O + row * D + 4 * part);
+        const f32x4 d = *(const f32x4*)(dO + row * D + 4 * part);
+        x = o[0] * d[0] + o[1] * d[1] + o[2] * d[2] + o[3] * d[3];
+        *(f32x4*)(dQ + row * D + 4 * part) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m);
+    if (row < rows && part == 0) Delta[row] = x;
+}
+
+// ---------------------------------------------------------------------------
+// 2. main KV-parallel kernel
+// ---------------------------------------------------------------------------
+template <int D>
+struct BwdTraits {
+    static constexpr int BM = 64;                   // query rows per tile
+    static constexpr int BN = 64;                   // keys per work-group (16 per wave)
+    static constexpr int NT = 256;
+    static constexpr int W = D >= 16 ? 4 : 2;       // contiguous head-dim values per fragment load
+    static constexpr int KSTEPS = D / 4;
+    static constexpr int DP = D >= 16 ? D : 16;     // head dim padded to whole 16-row tiles
+    static constexpr int NDT = DP / 16;
+    static constexpr int LD = DP + 4;               // LDS row stride of Q, dO, K tiles
+    static constexpr int LDS_ = BN + 4;             // LDS row stride of the dS tile
+    static constexpr int TILE4 = BM * D / 4;
+    static constexpr int PER = (TILE4 + NT - 1) / NT;
+};
+
+template <int W>
+__device__ __forceinline__ constexpr int frag_dim_b(int s, int g) {
+    return 4 * W * (s / W) + W * g + (s % W);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_main_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
+    int nkb, int nbkv, float scale, float c2 /* scale * log2(e) */) {
+    using Tr = BwdTraits<D>;
+    __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
+    __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
+    __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LD];
+    __shared__ __attribute__((aligned(16))) float dSs[Tr::BM * Tr::LDS_];
+    __shared__ float lse2s[Tr::BM];
+    __shared__ float dls[Tr::BM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = wave_uniform(tid >> 6);
+    const int li = lane & 15;
+    const int g = lane >> 4;
+
+    const int id = blockIdx.x;
+    const int kb = id / nbkv;  // key block 0 has the most query tiles: issued first
+    const int bkv = id % nbkv;
+    const int b = bkv / Hkv;
+    const int hk = bkv % Hkv;
+    const int G = Hq / Hkv;
+    const int nqb = (T + Tr::BM - 1) / Tr::BM;
+    const int kv0 = kb * Tr::BN;
+    const int keyw = kv0 + 16 * w + li;  // this lane's key (column of the S / dP tiles)
+
+    const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
+    const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
+
+    if constexpr (Tr::DP != D) {  // padding columns of the Q, dO, K tiles stay zero
+        for (int idx = tid; idx < Tr::BM * (Tr::DP - D); idx += Tr::NT) {
+            const int row = idx / (Tr::DP - D), col = D + idx % (Tr::DP - D);
+            Qs[row * Tr::LD + col] = 0.f;
+            dOs[row * Tr::LD + col] = 0.f;
+            Ks[row * Tr::LD + col] = 0.f;
+        }
+    }
+
+    // K, V fragments of this lane's key: slot s holds [keyw][frag_dim_b(s, g)]
+    float kf[Tr::KSTEPS], vf[Tr::KSTEPS];
+#pragma unroll
+    for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+        const int d0 = 4 * Tr::W * u + Tr::W * g;
+        if constexpr (Tr::W == 4) {
+            f32x4 x = keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 y = keyw < T ? *(const f32x4*)(Vh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kf[4 * u + j] = x[j];
+                vf[4 * u + j] = y[j];
+            }
+        } else {
+            f32x2 x = keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+            f32x2 y = keyw < T ? *(const f32x2*)(Vh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+            kf[2 * u] = x[0];
+            kf[2 * u + 1] = x[1];
+            vf[2 * u] = y[0];
+            vf[2 * u + 1] = y[1];
+        }
+    }
+    // the key block's K tile in LDS (B operand of dQ = dS K)
+    for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
+        const int row = idx / (D / 4), c4 = idx % (D / 4);
+        const int key = kv0 + row;
+        *(f32x4*)&Ks[row * Tr::LD + 4 * c4] =
+            key < T ? *(const f32x4*)(Kh + (size_t)key * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    f32x4 dk[Tr::NDT], dv[Tr::NDT];
+#pragma unroll
+    for (int dt = 0; dt < Tr::NDT; ++dt) {
+        dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    for (int hh = 0; hh < G; ++hh) {
+        const int h = hk * G + hh;
+        const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
+        const float* Qh = Q + hoff * D;
+        const float* dOh = dO + hoff * D;
+        float* dQh = dQ + hoff * D;
+
+        for (int qb = kb; qb < nqb; ++qb) {
+            const int q0 = qb * Tr::BM;
+            __syncthreads();  // the previous tile's LDS readers are done
+            for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
+                const int row = idx / (D / 4), c4 = idx % (D / 4);
+                const int q = q0 + row;
+                f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = x;
+                if (q < T) {
+                    x = *(const f32x4*)(Qh + (size_t)q * D + 4 * c4);
+                    y = *(const f32x4*)(dOh + (size_t)q * D + 4 * c4);
+                }
+                *(f32x4*)&Qs[row * Tr::LD + 4 * c4] = x;
+                *(f32x4*)&dOs[row * Tr::LD + 4 * c4] = y;
+            }
+            if (tid < Tr::BM) {
+                const int q = q0 + tid;
+                // a padding row gets LSE = +inf, so its probabilities are exactly 0
+                lse2s[tid] = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
+                dls[tid] = q < T ? Delta[hoff + q] : 0.f;
+            }
+            __syncthreads();
+
+            const bool diag = (qb == kb);
+            const int qs0 = diag ? w : 0;  // on the diagonal, query sub-tiles above this wave's keys are all masked
+
+            // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li]
+            f32x4 sa[4], pa[4];
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+                sa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+                pa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (qs >= qs0) {
+#pragma unroll
+                    for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+                        const int off = (16 * qs + li) * Tr::LD + 4 * Tr::W * u + Tr::W * g;
+                        if constexpr (Tr::W == 4) {
+                            const f32x4 a = *(const f32x4*)&Qs[off];
+                            const f32x4 c = *(const f32x4*)&dOs[off];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                sa[qs] = mfma16x16x4(a[j], kf[4 * u + j], sa[qs]);
+                                pa[qs] = mfma16x16x4(c[j], vf[4 * u + j], pa[qs]);
+                            }
+                        } else {
+                            const f32x2 a = *(const f32x2*)&Qs[off];
+                            const f32x2 c = *(const f32x2*)&dOs[off];
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                sa[qs] = mfma16x16x4(a[j], kf[2 * u + j], sa[qs]);
+                                pa[qs] = mfma16x16x4(c[j], vf[2 * u + j], pa[qs]);
+                            }
+                        }
+                    }
+                }
+            }
+
+            // P = exp(s - LSE) (0 where masked), dS = scale * P * (dP - Delta)
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int qr = 16 * qs + 4 * g + r;  // row within the tile
+                    float p = exp2_hw(sa[qs][r] * c2 - lse2s[qr]);
+                    if (qs < qs0 || (diag && 16 * w + li > qr)) p = 0.f;
+                    const float ds = scale * p * (pa[qs][r] - dls[qr]);
+                    sa[qs][r] = p;
+                    pa[qs][r] = ds;
+                }
+            }
+
+            // dV^T += dO^T P and dK^T += Q^T dS : k-step (qs, r) pairs lane row g with query 16qs + 4g + r
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs) {
+                if (qs >= qs0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = (16 * qs + 4 * g + r) * Tr::LD + li;
+#pragma unroll
+                        for (int dt = 0; dt < Tr::NDT; ++dt) {
+                            dv[dt] = mfma16x16x4(dOs[row + 16 * dt], sa[qs][r], dv[dt]);
+                            dk[dt] = mfma16x16x4(Qs[row + 16 * dt], pa[qs][r], dk[dt]);
+                        }
+                    }
+                }
+            }
+
+            // dS -> LDS as [query][key]
+#pragma unroll
+            for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dSs[(16 * qs + 4 * g + r) * Tr::LDS_ + 16 * w + li] = pa[qs][r];
+            __syncthreads();
+
+            // dQ rows 16w .. 16w+15 of the tile: C[query 16w + 4g + r][dim 16dt + li]
+            // k-step (u, j) pairs lane row g with key 16u + 4g + j; on the diagonal the
+            // key groups u > w are entirely above these rows (dS = 0 there)
+            const int u1 = diag ? w + 1 : 4;
+            f32x4 qa[Tr::NDT];
+#pragma unroll
+            for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (u < u1) {
+                    const f32x4 a = *(const f32x4*)&dSs[(16 * w + li) * Tr::LDS_ + 16 * u + 4 * g];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float* kp = &Ks[(16 * u + 4 * g + j) * Tr::LD + li];
+#pragma unroll
+                        for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = mfma16x16x4(a[j], kp[16 * dt], qa[dt]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < Tr::NDT; ++dt) {
+                const int d = 16 * dt + li;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int q = q0 + 16 * w + 4 * g + r;
+                    if (q < T && (Tr::DP == D || d < D)) unsafeAtomicAdd(dQh + (size_t)q * D + d, qa[dt][r]);
+                }
+            }
+        }
+    }
+
+    // dK, dV of this lane's key: C[dim 16dt + 4g + r][key li]
+    if (keyw < T) {
+        float* dKh = dK + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)keyw * D;
+        float* dVh = dV + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)keyw * D;
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) {
+            const int d0 = 16 * dt + 4 * g;
+            if (Tr::DP == D || d0 < D) {
+                *(f32x4*)(dKh + d0) = dk[dt];
+                *(f32x4*)(dVh + d0) = dv[dt];
+            }
+        }
+    }
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
+    using Tr = BwdTraits<D>;
+    const int64_t rows = a.B * a.Hq * a.T;
+    constexpr int RPB = 256 / (D / 4);
+    hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       stream, a.o, a.dout, a.delta, a.dq, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkb = (int)((a.T + Tr::BN - 1) / Tr::BN);
+    const int nbkv = (int)(a.B * a.Hkv);
+    hipLaunchKernelGGL(attn_bwd_main_kernel<D>, dim3((unsigned)(nkb * nbkv)), dim3(Tr::NT), 0, stream, a.q,
+                       a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
+                       nbkv, a.scale, a.scale * kLog2e);
+    return hipGetLastError();
+}
+
+size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t T) { return (size_t)(B * Hq * T); }
+
+hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 8: return launch_bwd_d<8>(a, stream);
+        case 16: return launch_bwd_d<16>(a, stream);
+        case 32: return launch_bwd_d<32>(a, stream);
+        case 64: return launch_bwd_d<64>(a, stream);
+        case 128: return launch_bwd_d<128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

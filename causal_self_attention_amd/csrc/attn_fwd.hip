@@ -1,0 +1,253 @@
+// Causal flash-style forward on gfx950: O = softmax(scale Q K^T, t_k <= t_q) V
+// and the per-row log-sum-exp, in memory linear in T.
+//
+// What is computed: "Architecture", "Tensor conventions" (row-major [B,H,T,D],
+// key t_k excluded when t_k > t_q) and "Intentional limits" (an exact
+// memory-linear path that keeps only per-row statistics); "Execution Backends
+// and the Python ABI", "What the Metal slice does" (the Flash forward saves row
+// maxima and exponential sums -- here folded into one log-sum-exp per row).
+//
+// Work decomposition (MI355X-first; the pages' tile-8 kernels are not reused):
+//   * one work-group = 4 waves = 64 query rows of one (batch, query head);
+//     wave w owns rows q0+16w .. q0+16w+15;
+//   * K/V tiles of 64 keys are staged in LDS through registers (the next tile's
+//     global loads are in flight while the current tile is multiplied);
+//   * each wave computes S^T = K Q^T on fp32 MFMA (16x16x4) with its Q rows held
+//     in registers, so a C tile has the query in the lane (i) and the keys in
+//     (g, r): the online-softmax statistics of a query stay in its four lanes;
+//   * P^T is then exactly the B operand of O^T += V^T P^T (keys are contracted
+//     in the permuted order (g, r), and V rows are read from LDS in that order);
+//   * only tiles with keys <= the block's last query are visited, and in the
+//     diagonal tile wave w skips the 16-key sub-tiles wholly above its rows;
+//   * blocks are issued heaviest first (longest causal prefix), which balances
+//     the triangular work over the CUs.
+#include "attn_launch.h"
+#include "device_common.h"
+
+namespace attn {
+
+template <int D>
+struct FwdTraits {
+    static constexpr int BM = 64;                     // query rows per work-group
+    static constexpr int BN = 64;                     // keys per K/V tile
+    static constexpr int NT = 256;                    // threads per work-group
+    static constexpr int W = D >= 16 ? 4 : 2;         // contiguous head-dim values per lane in a fragment
+    static constexpr int KSTEPS = D / 4;              // MFMA k-steps over the head dim
+    static constexpr int DP = D >= 16 ? D : 16;       // head dim padded to whole 16-row O^T tiles
+    static constexpr int NDT = DP / 16;               // O^T tiles per wave
+    static constexpr int LDK = D + 4;                 // LDS row stride of the K tile (floats)
+    static constexpr int LDV = DP + 4;                // LDS row stride of the V tile (floats)
+    static constexpr int TILE4 = BN * D / 4;          // float4 loads per K (or V) tile
+    static constexpr int PER = (TILE4 + NT - 1) / NT; // float4 loads per thread per tile
+};
+
+// Head-dim index of fragment slot s held by lane row g: groups of W contiguous
+// values per lane so that fragments load as one vector.
+template <int W>
+__device__ __forceinline__ constexpr int frag_dim(int s, int g) {
+    return 4 * W * (s / W) + W * g + (s % W);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int T, int nqb, int nbh,
+    float c2 /* scale * log2(e) */) {
+    using Tr = FwdTraits<D>;
+    __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LDK];
+    __shared__ __attribute__((aligned(16))) float Vs[Tr::BN * Tr::LDV];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = wave_uniform(tid >> 6);
+    const int li = lane & 15;
+    const int g = lane >> 4;
+
+    const int id = blockIdx.x;
+    const int qb = nqb - 1 - id / nbh;  // heaviest blocks first
+    const int bh = id % nbh;
+    const int b = bh / Hq;
+    const int h = bh % Hq;
+    const int hk = h / (Hq / Hkv);
+    const float* Qh = Q + ((size_t)b * Hq + h) * (size_t)T * D;
+    const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
+    const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
+    const int q0 = qb * Tr::BM;
+    const int qrow = q0 + 16 * w + li;  // this lane's query row
+
+    if constexpr (Tr::DP != D) {  // zero the padding columns of V once
+        for (int idx = tid; idx < Tr::BN * (Tr::DP - D); idx += Tr::NT) {
+            const int row = idx / (Tr::DP - D), col = D + idx % (Tr::DP - D);
+            Vs[row * Tr::LDV + col] = 0.f;
+        }
+    }
+
+    // Q fragments: slot s holds Q[qrow][frag_dim(s, g)]  (B operand of K Q^T)
+    float qf[Tr::KSTEPS];
+#pragma unroll
+    for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+        const int d0 = 4 * Tr::W * u + Tr::W * g;
+        if constexpr (Tr::W == 4) {
+            f32x4 x = qrow < T ? *(const f32x4*)(Qh + (size_t)qrow * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) qf[4 * u + j] = x[j];
+        } else {
+            f32x2 x = qrow < T ? *(const f32x2*)(Qh + (size_t)qrow * D + d0) : f32x2{0.f, 0.f};
+            qf[2 * u] = x[0];
+            qf[2 * u + 1] = x[1];
+        }
+    }
+
+    f32x4 acc[Tr::NDT];
+#pragma unroll
+    for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;  // running row max, log2 units
+    float l_run = 0.f;        // this lane's part of the running row sum
+
+    f32x4 kreg[Tr::PER], vreg[Tr::PER];
+    auto gload = [&](int kv0) {
+#pragma unroll
+        for (int i = 0; i < Tr::PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
+                const int row = idx / (D / 4), c4 = idx % (D / 4);
+                const int key = kv0 + row;
+                if (key < T) {
+                    kreg[i] = *(const f32x4*)(Kh + (size_t)key * D + 4 * c4);
+                    vreg[i] = *(const f32x4*)(Vh + (size_t)key * D + 4 * c4);
+                } else {
+                    kreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    vreg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < Tr::PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
+                const int row = idx / (D / 4), c4 = idx % (D / 4);
+                *(f32x4*)&Ks[row * Tr::LDK + 4 * c4] = kreg[i];
+                *(f32x4*)&Vs[row * Tr::LDV + 4 * c4] = vreg[i];
+            }
+        }
+    };
+
+    const int ntiles = qb + 1;  // BN == BM: tiles 0 .. qb, the last one diagonal
+    gload(0);
+    for (int j = 0; j < ntiles; ++j) {
+        __syncthreads();  // everyone is done reading the previous tile
+        lstore();
+        __syncthreads();
+        if (j + 1 < ntiles) gload((j + 1) * Tr::BN);
+
+        const int kv0 = j * Tr::BN;
+        const bool diag = (j == qb);
+        const int nsub = diag ? w + 1 : 4;  // 16-key sub-tiles with any key <= this wave's rows
+
+        // S^T = K Q^T : st[t] holds S^T[key = kv0 + 16t + 4g + r][query = qrow]
+        f32x4 st[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (t < nsub) {
+#pragma unroll
+                for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+                    const float* kp = &Ks[(16 * t + li) * Tr::LDK + 4 * Tr::W * u + Tr::W * g];
+                    if constexpr (Tr::W == 4) {
+                        const f32x4 a = *(const f32x4*)kp;
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) st[t] = mfma16x16x4(a[jj], qf[4 * u + jj], st[t]);
+                    } else {
+                        const f32x2 a = *(const f32x2*)kp;
+                        st[t] = mfma16x16x4(a[0], qf[2 * u], st[t]);
+                        st[t] = mfma16x16x4(a[1], qf[2 * u + 1], st[t]);
+                    }
+                }
+            }
+        }
+
+        // mask, scale to log2 units, row max over the 64 keys
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = kv0 + 16 * t + 4 * g + r;
+                float x = st[t][r] * c2;
+                if (t >= nsub || (diag && key > qrow)) x = -INFINITY;
+                st[t][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        }
+        mx = rows4_max(mx);
+        const float m_new = fmaxf(m_run, mx);  // finite: key kv0 <= qrow is always visible
+        const float alpha = exp2_hw(m_run - m_new);
+        m_run = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = exp2_hw(st[t][r] - m_new);
+                st[t][r] = p;
+                psum += p;
+            }
+        }
+        l_run = l_run * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] *= alpha;
+
+        // O^T += V^T P^T : k-step (t, r) pairs lane row g with key kv0 + 16t + 4g + r
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < nsub) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float* vp = &Vs[(16 * t + 4 * g + r) * Tr::LDV + li];
+#pragma unroll
+                    for (int dt = 0; dt < Tr::NDT; ++dt)
+                        acc[dt] = mfma16x16x4(vp[16 * dt], st[t][r], acc[dt]);
+                }
+            }
+        }
+    }
+
+    // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+    const float l_tot = rows4_sum(l_run);
+    const float inv = 1.f / l_tot;
+    if (qrow < T) {
+        float* Oh = O + ((size_t)b * Hq + h) * (size_t)T * D + (size_t)qrow * D;
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) {
+            const int d0 = 16 * dt + 4 * g;
+            if (Tr::DP == D || d0 < D) *(f32x4*)(Oh + d0) = acc[dt] * inv;
+        }
+        if (g == 0) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_run + log2_hw(l_tot)) * kLn2;
+    }
+}
+
+template <int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
+    using Tr = FwdTraits<D>;
+    const int nqb = (int)((a.T + Tr::BM - 1) / Tr::BM);
+    const int nbh = (int)(a.B * a.Hq);
+    const float c2 = a.scale * kLog2e;
+    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)(nqb * nbh)), dim3(Tr::NT), 0, stream, a.q, a.k,
+                       a.v, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.T, nqb, nbh, c2);
+    return hipGetLastError();
+}
+
+hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 8: return launch_fwd_d<8>(a, stream);
+        case 16: return launch_fwd_d<16>(a, stream);
+        case 32: return launch_fwd_d<32>(a, stream);
+        case 64: return launch_fwd_d<64>(a, stream);
+        case 128: return launch_fwd_d<128>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

@@ -1,0 +1,48 @@
+// Internal host-side launch interface between the C ABI (attn_api.cpp) and the
+// kernel translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+    const float *q, *k, *v;
+    float *o, *lse;
+    int64_t B, Hq, Hkv, T, D;
+    float scale;
+};
+
+struct BwdArgs {
+    const float *q, *k, *v, *o, *lse, *dout;
+    float *dq, *dk, *dv;
+    float* delta;  // workspace: [B, Hq, T]
+    int64_t B, Hq, Hkv, T, D;
+    float scale;
+};
+
+struct DecodeArgs {
+    const float *q, *k_pool, *v_pool;
+    const int32_t *block_table, *context_lens;
+    float *o, *lse;  // lse may be NULL
+    float* partial;  // workspace (see decode_workspace_floats)
+    int64_t S, Hq, Hkv, D, page_size, max_pages, num_pages;
+    float scale;
+};
+
+// Kernels exist for these head widths / page sizes.
+bool causal_head_dim_supported(int64_t D);
+bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group);
+
+// Workspace sizes in floats.
+size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t T);
+size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                               int64_t max_pages);
+
+hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,74 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// MFMA lane layout used throughout (v_mfma_f32_16x16x4_f32, one wave of 64
+// lanes, lane l = 16*g + i with i = l % 16 and g = l / 16):
+//   A (16x4, M x K): lane l holds A[m = i][k = g]
+//   B (4x16, K x N): lane l holds B[k = g][n = i]
+//   C (16x16):       lane l, register r holds C[m = 4*g + r][n = i]
+// so a C tile keeps its column index in i and spreads its rows over (g, r).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// 2^x and log2(x) on the hardware transcendental unit (v_exp_f32, v_log_f32).
+// exp(y) is evaluated as 2^(y * log2 e); the log2(e) factor is folded into the
+// score scale by the callers.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Both values {x[l], x[l ^ 16]} / {x[l], x[l ^ 32]} at every lane, through the
+// gfx950 row-swap permutes (no LDS traffic).  Only symmetric combinations of the
+// pair are used, so which element is which does not matter.
+__device__ __forceinline__ void pair_xor16(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows),
+// i.e. over g for a fixed i.  Every lane of the group ends with the same bits.
+__device__ __forceinline__ float rows4_max(float x) {
+    float a, b;
+    pair_xor16(x, a, b);
+    x = fmaxf(a, b);
+    pair_xor32(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    float a, b;
+    pair_xor16(x, a, b);
+    x = a + b;
+    pair_xor32(x, a, b);
+    return a + b;
+}
+
+// Reduction over the lanes of one 16-lane row (xor 1, 2, 4, 8).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace attn

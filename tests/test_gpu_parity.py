@@ -1,0 +1,349 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle.
+
+Tolerances (max-abs error relative to the reference's largest magnitude):
+O and LSE 1e-4, dQ/dK/dV 1e-3, paged decode vs dense decode 1e-5.
+
+Sizes the oracle finishes in seconds are compared element by element; the
+8192-token grouped-query forward is compared on sampled rows, each of which the
+oracle computes as a single-query decode over the row's causal prefix (the
+oracle's pins tie that decode to the last row of the causal forward).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_amd as attn
+import synthetic_inputs as si
+from gpu_common import TOL_DECODE, TOL_GRAD, TOL_LSE, TOL_O, announce, rel_err, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return require_gpu()
+
+
+def _to(d, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def _run_fwd(x, scale=None):
+    o, lse = attn.attn_causal_fwd(x["q"], x["k"], x["v"], scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _run_bwd(x, o, lse, scale=None):
+    dq, dk, dv = attn.attn_causal_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], scale=scale)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# the named causal workloads
+# ---------------------------------------------------------------------------
+FULL_WORKLOADS = ["mha_b1_h2_t16_d8", "mha_b8_h4_t256_d32", "mha_b4_h8_t1024_d64"]
+
+
+@pytest.mark.parametrize("name", FULL_WORKLOADS)
+def test_workload_forward_backward(dev, orc, name):
+    announce(f"fwd+bwd workload {name}")
+    host = si.causal_workload(name)
+    x = _to(host, dev)
+    D = host["q"].shape[-1]
+    scale = 1.0 / math.sqrt(D)
+    o, lse = _run_fwd(x, scale)
+    ro, rlse = orc.causal_fwd(host["q"], host["k"], host["v"], scale)
+    assert rel_err(o, ro) <= TOL_O, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_LSE, ("LSE", rel_err(lse, rlse))
+    dq, dk, dv = _run_bwd(x, o, lse, scale)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"], scale)
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+
+
+SAMPLE_ROWS = [0, 1, 15, 16, 63, 64, 65, 127, 128, 1000, 4095, 4096, 8127, 8128, 8190, 8191]
+
+
+def test_gqa_t8192_forward_sampled_rows(dev, orc):
+    name = "gqa_b1_hq16_hkv4_t8192_d64"
+    announce(f"fwd workload {name}")
+    host = si.causal_workload(name)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    o_h, lse_h = o.cpu(), lse.cpu()
+    assert torch.isfinite(o_h).all() and torch.isfinite(lse_h).all()
+    rng = np.random.default_rng(4)
+    rows = sorted(set(SAMPLE_ROWS) | set(int(r) for r in rng.integers(0, 8192, 24)))
+    q, k, v = host["q"][0], host["k"][0], host["v"][0]  # [H, T, D]
+    for i in rows:
+        ro, rlse = orc.decode_dense(q[:, i, :], k[:, : i + 1, :].transpose(0, 1), v[:, : i + 1, :].transpose(0, 1),
+                                    1.0 / 8.0)
+        assert rel_err(o_h[0, :, i, :], ro) <= TOL_O, ("O row", i, rel_err(o_h[0, :, i, :], ro))
+        assert rel_err(lse_h[0, :, i], rlse) <= TOL_LSE, ("LSE row", i)
+
+
+# ---------------------------------------------------------------------------
+# edge shapes: ragged tiles, every head width, grouped heads
+# ---------------------------------------------------------------------------
+EDGE_CASES = [(1, 2, 2, T, D) for D in (8, 16, 32, 64, 128) for T in (1, 17, 65, 129)]
+EDGE_CASES += [(2, 3, 3, 2, 64), (1, 1, 1, 15, 32), (1, 2, 1, 63, 64), (2, 4, 2, 200, 64),
+               (1, 4, 1, 100, 64), (1, 8, 1, 77, 32), (1, 8, 2, 130, 16), (1, 16, 2, 96, 128)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D", EDGE_CASES)
+def test_edge_shapes(dev, orc, B, Hq, Hkv, T, D):
+    announce(f"edge fwd+bwd B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    host = si.causal_inputs(B, Hq, Hkv, T, D, seed=1000 + T * 7 + D + Hq)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    ro, rlse = orc.causal_fwd(host["q"], host["k"], host["v"])
+    assert rel_err(o, ro) <= TOL_O and rel_err(lse, rlse) <= TOL_LSE, (rel_err(o, ro), rel_err(lse, rlse))
+    dq, dk, dv = _run_bwd(x, o, lse)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+
+
+def test_gqa_backward_long_context(dev, orc):
+    """Grouped heads (G = 4) through the backward at T = 1024."""
+    announce("gqa fwd+bwd B=1 Hq=16 Hkv=4 T=1024 D=64")
+    host = si.causal_inputs(1, 16, 4, 1024, 64, seed=44)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    ro, _ = orc.causal_fwd(host["q"], host["k"], host["v"])
+    assert rel_err(o, ro) <= TOL_O
+    dq, dk, dv = _run_bwd(x, o, lse)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms on the GPU outputs
+# ---------------------------------------------------------------------------
+def test_single_position_is_exact(dev):
+    announce("T=1 closed form")
+    host = si.causal_inputs(2, 4, 2, 1, 64, seed=7)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x, 0.3)
+    assert torch.equal(o.cpu(), host["v"].repeat_interleave(2, dim=1)), "T=1: O must equal V exactly"
+    want = 0.3 * (host["q"][:, :, 0].double() * host["k"].repeat_interleave(2, dim=1)[:, :, 0].double()).sum(-1)
+    assert rel_err(lse[:, :, 0], want) <= TOL_LSE
+    dq, dk, dv = _run_bwd(x, o, lse, 0.3)
+    # P = 1, so dS = dP - Delta is rounding noise only
+    assert float(dq.abs().max()) < 1e-4 and float(dk.abs().max()) < 1e-4
+    want_dv = host["dout"].reshape(2, 2, 2, 1, 64).sum(2)
+    assert rel_err(dv, want_dv) <= 1e-5
+
+
+def test_zero_scale_is_prefix_mean(dev):
+    announce("scale=0 prefix mean")
+    host = si.causal_inputs(1, 2, 2, 150, 32, seed=8)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x, 0.0)
+    cnt = torch.arange(1, 151, dtype=torch.float64)
+    want = torch.cumsum(host["v"].double(), dim=2) / cnt[None, None, :, None]
+    assert rel_err(o, want) <= TOL_O
+    assert rel_err(lse, torch.log(cnt).expand(1, 2, 150)) <= TOL_LSE
+    dq, dk, dv = _run_bwd(x, o, lse, 0.0)
+    assert float(dq.abs().max()) == 0.0 and float(dk.abs().max()) == 0.0
+
+
+def test_causality_is_bitwise(dev):
+    """Changing keys/values at positions >= s leaves rows < s unchanged, bit for bit."""
+    announce("causality")
+    host = si.causal_inputs(1, 4, 2, 300, 64, seed=9)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    for s in (5, 64, 100, 257):
+        y = dict(x)
+        k2, v2 = x["k"].clone(), x["v"].clone()
+        k2[:, :, s:] += 2.5
+        v2[:, :, s:] *= -3.0
+        y["k"], y["v"] = k2, v2
+        o2, lse2 = _run_fwd(y)
+        assert torch.equal(o2[:, :, :s], o[:, :, :s]), ("O", s)
+        assert torch.equal(lse2[:, :, :s], lse[:, :, :s]), ("LSE", s)
+        # NaN keys in the future are masked by selection, not arithmetic
+        k3 = x["k"].clone()
+        k3[:, :, s:] = float("nan")
+        y["k"], y["v"] = k3, x["v"]
+        o3, lse3 = _run_fwd(y)
+        assert torch.equal(o3[:, :, :s], o[:, :, :s]), ("NaN K", s)
+
+
+def test_gradient_sums(dev):
+    """Each dS row sums to zero, so sum_j dK_j = 0; sum_j dV_j = sum_i dO_i per group."""
+    announce("gradient sums")
+    host = si.causal_inputs(2, 4, 2, 190, 32, seed=10)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    dq, dk, dv = _run_bwd(x, o, lse)
+    dk_sum = dk.double().sum(2)
+    assert float(dk_sum.abs().max()) <= 1e-3 * float(dk.abs().max()) * math.sqrt(190)
+    want = host["dout"].double().sum(2).reshape(2, 2, 2, 32).sum(2)
+    assert rel_err(dv.double().sum(2), want) <= 1e-4
+
+
+def test_forward_is_deterministic(dev):
+    announce("forward determinism")
+    host = si.causal_inputs(2, 8, 2, 333, 64, seed=11)
+    x = _to(host, dev)
+    o1, l1 = _run_fwd(x)
+    o2, l2 = _run_fwd(x)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    dq1, dk1, dv1 = _run_bwd(x, o1, l1)
+    dq2, dk2, dv2 = _run_bwd(x, o1, l1)
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)  # dQ uses float atomics
+    assert rel_err(dq1, dq2) <= 1e-6
+
+
+def test_outputs_fully_overwritten(dev, orc):
+    """Outputs (including dQ) do not depend on what the buffers held before."""
+    announce("outputs overwritten")
+    host = si.causal_inputs(1, 2, 2, 70, 16, seed=12)
+    x = _to(host, dev)
+    o = torch.full_like(x["q"], float("nan"))
+    lse = torch.full((1, 2, 70), float("nan"), device=dev)
+    attn.attn_causal_fwd(x["q"], x["k"], x["v"], o=o, lse=lse)
+    dq = torch.full_like(x["q"], 7.0)
+    dk = torch.full_like(x["k"], float("nan"))
+    dv = torch.full_like(x["v"], float("nan"))
+    ws = torch.full((attn.attn_causal_bwd_workspace_bytes(1, 2, 2, 70, 16) // 4,), float("nan"), device=dev)
+    attn.attn_causal_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    ro, _ = orc.causal_fwd(host["q"], host["k"], host["v"])
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    assert rel_err(o, ro) <= TOL_O
+    for a, b in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD
+
+
+# ---------------------------------------------------------------------------
+# paged decode
+# ---------------------------------------------------------------------------
+def _decode(d, dev, scale=None, **kw):
+    o, lse = attn.attn_paged_decode(d["q"].to(dev), d["k_pool"].to(dev), d["v_pool"].to(dev),
+                                    d["block_table"].to(dev), d["context_lens"].to(dev), scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _contiguous_layout(d):
+    """Same sequences, pages laid out in logical order with identity-like tables."""
+    bt, ctx, ps = d["block_table"], d["context_lens"], d["page_size"]
+    S = bt.shape[0]
+    pages, rows = [], torch.full_like(bt, 0)
+    off = 0
+    for s in range(S):
+        n = math.ceil(int(ctx[s]) / ps)
+        pages.append(bt[s, :n].long())
+        rows[s, :n] = torch.arange(off, off + n, dtype=torch.int32)
+        off += n
+    idx = torch.cat(pages + [torch.tensor([d["poison_page"]])])
+    for s in range(S):
+        n = math.ceil(int(ctx[s]) / ps)
+        rows[s, n:] = off  # padding -> the copied poison page
+    out = dict(d)
+    out["k_pool"] = d["k_pool"][idx].contiguous()
+    out["v_pool"] = d["v_pool"][idx].contiguous()
+    out["block_table"] = rows
+    return out
+
+
+def test_decode_workload(dev, orc):
+    name = next(iter(si.DECODE_WORKLOADS))
+    announce(f"decode workload {name}")
+    d = si.decode_workload(name)
+    o, lse = _decode(d, dev)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE, ("LSE", rel_err(lse, rlse))
+    # the same kernel on a contiguous copy of the gathered sequences: identical bits
+    c = _contiguous_layout(d)
+    o2, lse2 = _decode(c, dev)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_decode_poisoned_tail_and_padding(dev):
+    """NaN in pool slots past each context and in the padding page changes nothing."""
+    announce("decode poison")
+    d = si.paged_decode_inputs(S=9, Hq=16, Hkv=4, D=64, page_size=16, ctx_lo=1, ctx_hi=700, max_pages=48, seed=21)
+    o, lse = _decode(d, dev)
+    kp, vp = d["k_pool"].clone(), d["v_pool"].clone()
+    kp[d["poison_page"]] = float("nan")
+    vp[d["poison_page"]] = float("nan")
+    for s in range(9):
+        n = int(d["context_lens"][s])
+        last = int(d["block_table"][s, (n - 1) // 16])
+        kp[last, :, (n - 1) % 16 + 1:] = float("nan")
+        vp[last, :, (n - 1) % 16 + 1:] = float("nan")
+    p = dict(d)
+    p["k_pool"], p["v_pool"] = kp, vp
+    o2, lse2 = _decode(p, dev)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_decode_pool_permutation(dev):
+    announce("decode pool permutation")
+    d = si.paged_decode_inputs(S=6, Hq=8, Hkv=2, D=32, page_size=16, ctx_lo=100, ctx_hi=900, max_pages=64, seed=22)
+    o, lse = _decode(d, dev)
+    perm = torch.randperm(d["num_pages"], generator=torch.Generator().manual_seed(23))
+    p = dict(d)
+    kp = torch.empty_like(d["k_pool"])
+    vp = torch.empty_like(d["v_pool"])
+    kp[perm] = d["k_pool"]
+    vp[perm] = d["v_pool"]
+    p["k_pool"], p["v_pool"] = kp, vp
+    p["block_table"] = perm[d["block_table"].long()].to(torch.int32)
+    o2, lse2 = _decode(p, dev)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+DECODE_CASES = [(D, G, ps) for D in (8, 16, 32, 64, 128) for G in (1, 4) for ps in (16, 64)]
+DECODE_CASES += [(64, 8, 16), (32, 2, 32), (16, 8, 32)]
+
+
+@pytest.mark.parametrize("D,G,ps", DECODE_CASES)
+def test_decode_shapes(dev, orc, D, G, ps):
+    announce(f"decode D={D} G={G} page={ps}")
+    Hkv = 2
+    d = si.paged_decode_inputs(S=5, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=520,
+                               max_pages=math.ceil(520 / ps) + 1, seed=100 + D + G + ps)
+    d["context_lens"][0] = 1  # a single cached position
+    o, lse = _decode(d, dev)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE
+    # one position: the output is that position's value row
+    g_of = torch.arange(Hkv * G) // G
+    assert torch.equal(o[0].cpu(), d["v_pool"][int(d["block_table"][0, 0]), g_of, 0, :])
+    # without lse
+    o3, lse3 = _decode(d, dev, with_lse=False)
+    assert lse3 is None and torch.equal(o3, o)
+
+
+def test_decode_matches_causal_last_row(dev):
+    """Decode over a contiguous sequence equals the causal forward's last row."""
+    announce("decode vs causal last row")
+    T, D, Hq, Hkv = 300, 64, 8, 2
+    host = si.causal_inputs(1, Hq, Hkv, T, D, seed=31, with_do=False)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    ps = 16
+    npg = math.ceil(T / ps)
+    kp = torch.zeros(npg, Hkv, ps, D)
+    vp = torch.zeros(npg, Hkv, ps, D)
+    for t in range(T):
+        kp[t // ps, :, t % ps] = host["k"][0, :, t]
+        vp[t // ps, :, t % ps] = host["v"][0, :, t]
+    d = {"q": host["q"][0, :, T - 1].unsqueeze(0).contiguous(), "k_pool": kp, "v_pool": vp,
+         "block_table": torch.arange(npg, dtype=torch.int32).unsqueeze(0),
+         "context_lens": torch.tensor([T], dtype=torch.int32)}
+    od, lsed = _decode(d, dev)
+    assert rel_err(od[0], o[0, :, T - 1]) <= TOL_O
+    assert rel_err(lsed[0], lse[0, :, T - 1]) <= TOL_LSE
