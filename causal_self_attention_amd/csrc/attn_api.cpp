@@ -8,6 +8,7 @@
 // and all checks finish before the first HIP call.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -90,7 +91,11 @@ attn_status check_causal_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, in
     return ATTN_OK;
 }
 
-attn_status device_ready() {
+// Compute-unit count of each device, read once (0 = not read yet).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+attn_status device_ready(int* cu_count) {
     int n = 0;
     hipError_t e = hipGetDeviceCount(&n);
     if (e != hipSuccess || n <= 0)
@@ -99,6 +104,14 @@ attn_status device_ready() {
     int dev = -1;
     e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(ATTN_DEVICE_ERROR, std::string("no current HIP device: ") + hipGetErrorString(e));
+    int cu = (dev >= 0 && dev < kMaxDevices) ? g_cu_count[dev].load(std::memory_order_relaxed) : 0;
+    if (cu <= 0) {
+        e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cu <= 0)
+            return fail(ATTN_DEVICE_ERROR, std::string("cannot read the compute-unit count: ") + hipGetErrorString(e));
+        if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cu, std::memory_order_relaxed);
+    }
+    *cu_count = cu;
     return ATTN_OK;
 }
 
@@ -131,8 +144,9 @@ attn_status attn_causal_fwd(const float* q, const float* k, const float* v, int6
         const size_t qb = (size_t)(B * Hq * T * D) * 4, kb = (size_t)(B * Hkv * T * D) * 4;
         const size_t lb = (size_t)(B * Hq * T) * 4;
         ATTN_TRY(check_disjoint({{o, qb, "o"}, {lse, lb, "lse"}}, {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
-        ATTN_TRY(device_ready());
-        attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, T, D, scale};
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, T, D, scale, cus};
         return launched(attn::launch_causal_fwd(a, (hipStream_t)stream), "attn_causal_fwd launch");
     } catch (const std::exception& e) {
         return fail(ATTN_DEVICE_ERROR, std::string("attn_causal_fwd: ") + e.what());
@@ -172,8 +186,9 @@ attn_status attn_causal_bwd(const float* q, const float* k, const float* v, cons
         ATTN_TRY(check_disjoint({{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"}},
                                 {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {lse, lb, "lse"},
                                  {dout, qb, "dout"}}));
-        ATTN_TRY(device_ready());
-        attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, Hq, Hkv, T, D, scale};
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, Hq, Hkv, T, D, scale, cus};
         return launched(attn::launch_causal_bwd(a, (hipStream_t)stream), "attn_causal_bwd launch");
     } catch (const std::exception& e) {
         return fail(ATTN_DEVICE_ERROR, std::string("attn_causal_bwd: ") + e.what());
@@ -209,7 +224,7 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
             return fail(ATTN_UNSUPPORTED, "no decode kernel for D=" + std::to_string(D) + ", page_size=" +
                                               std::to_string(page_size) + ", Hq/Hkv=" + std::to_string(Hq / Hkv) +
                                               " (supported: D in {8,16,32,64,128}, page_size in {16,32,64}, "
-                                              "Hq/Hkv in {1,2,4,8} with Hq/Hkv*D <= 512)");
+                                              "1 <= Hq/Hkv <= 16)");
         ATTN_TRY(check_ptr(q, "q", 16));
         ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
         ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
@@ -228,7 +243,8 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
         ATTN_TRY(check_disjoint({{o, qb, "o"}, lr, {workspace, need, "workspace"}},
                                 {{q, qb, "q"}, {k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
                                  {block_table, tb, "block_table"}, {context_lens, cb, "context_lens"}}));
-        ATTN_TRY(device_ready());
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
         attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, (float*)workspace,
                            S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale};
         return launched(attn::launch_paged_decode(a, (hipStream_t)stream), "attn_paged_decode launch");

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
-    int nkb, int nbkv, float scale, float c2 /* scale * log2(e) */) {
+    int nkb, int nbkv, int ncu, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
@@ -96,9 +96,9 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
     const int li = lane & 15;
     const int g = lane >> 4;
 
-    const int id = blockIdx.x;
-    const int kb = id / nbkv;  // key block 0 has the most query tiles: issued first
-    const int bkv = id % nbkv;
+    const int rank = snake_rank(blockIdx.x, nkb * nbkv, ncu);
+    const int kb = rank / nbkv;  // key block 0 has the most query tiles: rank 0
+    const int bkv = rank % nbkv;
     const int b = bkv / Hkv;
     const int hk = bkv % Hkv;
     const int G = Hq / Hkv;
@@ -312,9 +312,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int nkb = (int)((a.T + Tr::BN - 1) / Tr::BN);
     const int nbkv = (int)(a.B * a.Hkv);
+    const int n = nkb * nbkv;
+    const int ncu = n <= 2 * a.cu_count ? a.cu_count : n;  // snake only when all groups are resident
     hipLaunchKernelGGL(attn_bwd_main_kernel<D>, dim3((unsigned)(nkb * nbkv)), dim3(Tr::NT), 0, stream, a.q,
                        a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
-                       nbkv, a.scale, a.scale * kLog2e);
+                       nbkv, ncu, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@
 //     in the permuted order (g, r), and V rows are read from LDS in that order);
 //   * only tiles with keys <= the block's last query are visited, and in the
 //     diagonal tile wave w skips the 16-key sub-tiles wholly above its rows;
-//   * blocks are issued heaviest first (longest causal prefix), which balances
-//     the triangular work over the CUs.
+//   * blocks are ranked heaviest first (longest causal prefix) and dealt to the
+//     CUs in snake order (see snake_rank), which balances the triangular work.
 #include "attn_launch.h"
 #include "device_common.h"
 
@@ -51,7 +51,7 @@ __device__ __forceinline__ constexpr int frag_dim(int s, int g) {
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int T, int nqb, int nbh,
+    float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int T, int nqb, int nbh, int ncu,
     float c2 /* scale * log2(e) */) {
     using Tr = FwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LDK];
@@ -63,9 +63,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const int li = lane & 15;
     const int g = lane >> 4;
 
-    const int id = blockIdx.x;
-    const int qb = nqb - 1 - id / nbh;  // heaviest blocks first
-    const int bh = id % nbh;
+    const int rank = snake_rank(blockIdx.x, nqb * nbh, ncu);
+    const int qb = nqb - 1 - rank / nbh;  // rank 0 = the longest causal prefix
+    const int bh = rank % nbh;
     const int b = bh / Hq;
     const int h = bh % Hq;
     const int hk = h / (Hq / Hkv);
@@ -234,8 +234,12 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
     const int nqb = (int)((a.T + Tr::BM - 1) / Tr::BM);
     const int nbh = (int)(a.B * a.Hq);
     const float c2 = a.scale * kLog2e;
+    // snake order only pays when every work-group is resident at once (two per CU);
+    // for longer grids plain heaviest-first order is kept (a round as long as the grid)
+    const int n = nqb * nbh;
+    const int ncu = n <= 2 * a.cu_count ? a.cu_count : n;
     hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)(nqb * nbh)), dim3(Tr::NT), 0, stream, a.q, a.k,
-                       a.v, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.T, nqb, nbh, c2);
+                       a.v, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.T, nqb, nbh, ncu, c2);
     return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ struct FwdArgs {
     float *o, *lse;
     int64_t B, Hq, Hkv, T, D;
     float scale;
+    int cu_count;  // compute units of the device (work ordering)
 };
 
 struct BwdArgs {
@@ -21,6 +22,7 @@ struct BwdArgs {
     float* delta;  // workspace: [B, Hq, T]
     int64_t B, Hq, Hkv, T, D;
     float scale;
+    int cu_count;
 };
 
 struct DecodeArgs {
@@ -31,6 +33,17 @@ struct DecodeArgs {
     int64_t S, Hq, Hkv, D, page_size, max_pages, num_pages;
     float scale;
 };
+
+// Work ordering for triangular (causal) grids.  Work items are ranked heaviest
+// first; work-group ids are dealt to the compute units in rounds of `ncu`, and
+// every second round is reversed, so the work-groups that end up sharing a
+// compute unit pair heavy items with light ones.  Returns the rank of `id`.
+__device__ __forceinline__ int snake_rank(int id, int n, int ncu) {
+    const int round = id / ncu;
+    const int base = round * ncu;
+    const int m = n - base < ncu ? n - base : ncu;
+    return (round & 1) ? base + (m - 1 - (id - base)) : id;
+}
 
 // Kernels exist for these head widths / page sizes.
 bool causal_head_dim_supported(int64_t D);

@@ -60,14 +60,40 @@ __device__ __forceinline__ float rows4_sum(float x) {
     return a + b;
 }
 
-// Reduction over the lanes of one 16-lane row (xor 1, 2, 4, 8).
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
-    return x;
+// Data-parallel-primitive lane moves (VALU, no LDS): CTRL is the DPP control.
+//   0xB1 quad_perm [1,0,3,2] = lane ^ 1        0x4E quad_perm [2,3,0,1] = lane ^ 2
+//   0x124 row_ror:4, 0x128 row_ror:8 (rotate inside a 16-lane row; lane % 4 kept)
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor8 = 0x128;
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7 - i inside each 8-lane half-row
+
+// sum / max over the 4 lanes of a quad (lanes 4k .. 4k+3)
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp_mov<kDppXor1>(x);
+    return x + dpp_mov<kDppXor2>(x);
+}
+__device__ __forceinline__ float quad_max(float x) {
+    x = fmaxf(x, dpp_mov<kDppXor1>(x));
+    return fmaxf(x, dpp_mov<kDppXor2>(x));
+}
+// sum / max over the 4 lanes of a 16-lane row that share lane % 4
+__device__ __forceinline__ float row_stride4_sum(float x) {
+    x += dpp_mov<kDppRor4>(x);
+    return x + dpp_mov<kDppRor8>(x);
+}
+__device__ __forceinline__ float row_stride4_max(float x) {
+    x = fmaxf(x, dpp_mov<kDppRor4>(x));
+    return fmaxf(x, dpp_mov<kDppRor8>(x));
+}
+// whole-wave reductions
+__device__ __forceinline__ float wave_sum(float x) { return rows4_sum(row_stride4_sum(quad_sum(x))); }
+__device__ __forceinline__ float wave_max(float x) { return rows4_max(row_stride4_max(quad_max(x))); }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

@@ -66,8 +66,9 @@ uint32_t attn_abi_version(void);
  * pointer stays valid until the next attn_* call on the same thread. */
 const char* attn_last_error(void);
 
-/* Supported head widths: D in {8, 16, 32, 64, 128} for the causal calls and
- * D in {8, 16, 32, 64, 128} for decode; page_size in {16, 32, 64}. */
+/* Kernels exist for head widths D in {8, 16, 32, 64, 128} (all calls), decode
+ * page sizes in {16, 32, 64} and decode group sizes 1 <= Hq/Hkv <= 16; other
+ * values return ATTN_UNSUPPORTED. */
 
 /*
  * Causal forward.

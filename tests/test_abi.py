@@ -68,8 +68,10 @@ def test_workspace_queries(L):
     assert attn.attn_causal_bwd_workspace_bytes(1, 3, 2, 16, 8) == 0    # Hq % Hkv != 0
     assert attn.attn_causal_bwd_workspace_bytes(0, 2, 2, 16, 8) == 0
     ws = attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 256)
-    chunks = math.ceil(16 * 256 / 128)
-    assert ws == math.ceil(32 * 16 * chunks * (64 + 2) * 4 / 256) * 256
+    # partial (m, l, o[D]) records per sequence, query head and chunk, 256-byte rounded
+    assert ws % 256 == 0 and ws >= 32 * 16 * (64 + 2) * 4
+    assert attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 512) > ws
+    assert attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 1) >= 32 * 16 * (64 + 2) * 4
     assert attn.attn_paged_decode_workspace_bytes(32, 16, 5, 64, 16, 256) == 0
 
 
@@ -144,7 +146,7 @@ def test_decode_invalid_arguments(L):
     _expect(_dec(L, Hq=6, Hkv=4), attn.ATTN_INVALID_ARGUMENT, "Hq % Hkv")
     _expect(_dec(L, page=8), attn.ATTN_UNSUPPORTED, "page_size=8")
     _expect(_dec(L, D=48), attn.ATTN_UNSUPPORTED, "D=48")
-    _expect(_dec(L, Hq=32, Hkv=2), attn.ATTN_UNSUPPORTED, "Hq/Hkv=16")
+    _expect(_dec(L, Hq=34, Hkv=2), attn.ATTN_UNSUPPORTED, "Hq/Hkv=17")
     _expect(_dec(L, scale=float("nan")), attn.ATTN_INVALID_ARGUMENT, "scale")
     _expect(_dec(L, ws_bytes=1), attn.ATTN_WORKSPACE_TOO_SMALL, "needs")
     _expect(_dec(L, o=_p(1)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'k_pool'")
