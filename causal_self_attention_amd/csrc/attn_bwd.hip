@@ -20,7 +20,9 @@
 //      Q and dO staged in LDS):
 //        S  = Q K^T, dP = dO V^T           (C tiles: key in the lane i)
 //        P, dS                             (elementwise, masked on the diagonal)
-//        dV^T += dO^T P,  dK^T += Q^T dS   (P and dS are the B operands as-is)
+//        dV += P^T dO,  dK += dS^T Q       (P and dS are the A operands as-is; the
+//                                           dO and Q rows load as vectors because
+//                                           lane i owns dims NDT*i .. NDT*i+NDT-1)
 //        dS -> LDS, then dQ(16 rows per wave) = dS K, added to dQ with float
 //        atomics (the contraction runs over the whole 64-key block).
 #include "attn_launch.h"
@@ -63,17 +65,35 @@ struct BwdTraits {
     static constexpr int NT = 256;
     static constexpr int W = D >= 16 ? 4 : 2;       // contiguous head-dim values per fragment load
     static constexpr int KSTEPS = D / 4;
-    static constexpr int DP = D >= 16 ? D : 16;     // head dim padded to whole 16-row tiles
-    static constexpr int NDT = DP / 16;
+    static constexpr int DP = D >= 16 ? D : 16;     // head dim padded to whole 16-column tiles
+    static constexpr int NDT = DP / 16;             // C tiles over the head dim
     static constexpr int LD = DP + 4;               // LDS row stride of Q, dO, K tiles
     static constexpr int LDS_ = BN + 4;             // LDS row stride of the dS tile
     static constexpr int TILE4 = BM * D / 4;
-    static constexpr int PER = (TILE4 + NT - 1) / NT;
 };
 
 template <int W>
 __device__ __forceinline__ constexpr int frag_dim_b(int s, int g) {
     return 4 * W * (s / W) + W * g + (s % W);
+}
+
+// NDT contiguous floats from LDS (one vector read when NDT is 2 or a multiple of 4)
+template <int N>
+__device__ __forceinline__ void lds_row(const float* p, float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const f32x4 v = *(const f32x4*)(p + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 * i + j] = v[j];
+        }
+    } else if constexpr (N == 2) {
+        const f32x2 v = *(const f32x2*)p;
+        x[0] = v[0];
+        x[1] = v[1];
+    } else {
+        x[0] = p[0];
+    }
 }
 
 template <int D>
@@ -87,8 +107,8 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dSs[Tr::BM * Tr::LDS_];
-    __shared__ float lse2s[Tr::BM];
-    __shared__ float dls[Tr::BM];
+    __shared__ __attribute__((aligned(16))) float lse2s[Tr::BM];
+    __shared__ __attribute__((aligned(16))) float dls[Tr::BM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -148,6 +168,7 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
             key < T ? *(const f32x4*)(Kh + (size_t)key * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // dK, dV accumulators as [key 4g + r][dim NDT*li + dt] (this wave's 16 keys)
     f32x4 dk[Tr::NDT], dv[Tr::NDT];
 #pragma unroll
     for (int dt = 0; dt < Tr::NDT; ++dt) {
@@ -184,8 +205,11 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
             }
             __syncthreads();
 
+            // Every sub-tile is computed, also on the diagonal where some lie wholly above
+            // this wave's keys: their probabilities are zeroed by the causal select below.
+            // Skipping them would put branches around accumulating MFMAs, and the compiler
+            // then copies the accumulators at every join, which costs more than it saves.
             const bool diag = (qb == kb);
-            const int qs0 = diag ? w : 0;  // on the diagonal, query sub-tiles above this wave's keys are all masked
 
             // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li]
             f32x4 sa[4], pa[4];
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
             for (int qs = 0; qs < 4; ++qs) {
                 sa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
                 pa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (qs >= qs0) {
+                {
 #pragma unroll
                     for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
                         const int off = (16 * qs + li) * Tr::LD + 4 * Tr::W * u + Tr::W * g;
@@ -218,31 +242,39 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
                 }
             }
 
-            // P = exp(s - LSE) (0 where masked), dS = scale * P * (dP - Delta)
+            // P = exp(s - LSE) (0 where masked), dS = scale * P * (dP - Delta).  Row
+            // statistics come in as one vector per sub-tile; the mask is a select.
 #pragma unroll
             for (int qs = 0; qs < 4; ++qs) {
+                const f32x4 l4 = *(const f32x4*)&lse2s[16 * qs + 4 * g];
+                const f32x4 d4 = *(const f32x4*)&dls[16 * qs + 4 * g];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int qr = 16 * qs + 4 * g + r;  // row within the tile
-                    float p = exp2_hw(sa[qs][r] * c2 - lse2s[qr]);
-                    if (qs < qs0 || (diag && 16 * w + li > qr)) p = 0.f;
-                    const float ds = scale * p * (pa[qs][r] - dls[qr]);
+                    float p = exp2_hw(sa[qs][r] * c2 - l4[r]);
+                    p = (diag && 16 * w + li > qr) ? 0.f : p;
+                    const float ds = scale * p * (pa[qs][r] - d4[r]);
                     sa[qs][r] = p;
                     pa[qs][r] = ds;
                 }
             }
 
-            // dV^T += dO^T P and dK^T += Q^T dS : k-step (qs, r) pairs lane row g with query 16qs + 4g + r
+            // dV += P^T dO and dK += dS^T Q with P, dS as the A operands straight from their
+            // accumulators (k-step (qs, r) pairs lane row g with query 16qs + 4g + r) and the
+            // dO / Q rows as B operands, lane li taking dims NDT*li .. NDT*li+NDT-1
 #pragma unroll
             for (int qs = 0; qs < 4; ++qs) {
-                if (qs >= qs0) {
+                {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = (16 * qs + 4 * g + r) * Tr::LD + li;
+                        const int row = (16 * qs + 4 * g + r) * Tr::LD + Tr::NDT * li;
+                        float bo[Tr::NDT], bq[Tr::NDT];
+                        lds_row<Tr::NDT>(&dOs[row], bo);
+                        lds_row<Tr::NDT>(&Qs[row], bq);
 #pragma unroll
                         for (int dt = 0; dt < Tr::NDT; ++dt) {
-                            dv[dt] = mfma16x16x4(dOs[row + 16 * dt], sa[qs][r], dv[dt]);
-                            dk[dt] = mfma16x16x4(Qs[row + 16 * dt], pa[qs][r], dk[dt]);
+                            dv[dt] = mfma16x16x4(sa[qs][r], bo[dt], dv[dt]);
+                            dk[dt] = mfma16x16x4(pa[qs][r], bq[dt], dk[dt]);
                         }
                     }
                 }
@@ -256,15 +288,13 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
             __syncthreads();
 
             // dQ rows 16w .. 16w+15 of the tile: C[query 16w + 4g + r][dim 16dt + li]
-            // k-step (u, j) pairs lane row g with key 16u + 4g + j; on the diagonal the
-            // key groups u > w are entirely above these rows (dS = 0 there)
-            const int u1 = diag ? w + 1 : 4;
+            // k-step (u, j) pairs lane row g with key 16u + 4g + j
             f32x4 qa[Tr::NDT];
 #pragma unroll
             for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                if (u < u1) {
+                {
                     const f32x4 a = *(const f32x4*)&dSs[(16 * w + li) * Tr::LDS_ + 16 * u + 4 * g];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
@@ -274,28 +304,45 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
                     }
                 }
             }
+            if (q0 + Tr::BM <= T && Tr::DP == D) {  // full tile: no per-element checks
 #pragma unroll
-            for (int dt = 0; dt < Tr::NDT; ++dt) {
-                const int d = 16 * dt + li;
+                for (int dt = 0; dt < Tr::NDT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int q = q0 + 16 * w + 4 * g + r;
-                    if (q < T && (Tr::DP == D || d < D)) unsafeAtomicAdd(dQh + (size_t)q * D + d, qa[dt][r]);
+                    for (int r = 0; r < 4; ++r)
+                        unsafeAtomicAdd(dQh + (size_t)(q0 + 16 * w + 4 * g + r) * D + 16 * dt + li, qa[dt][r]);
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; ++dt) {
+                    const int d = 16 * dt + li;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int q = q0 + 16 * w + 4 * g + r;
+                        if (q < T && (Tr::DP == D || d < D)) unsafeAtomicAdd(dQh + (size_t)q * D + d, qa[dt][r]);
+                    }
                 }
             }
         }
     }
 
-    // dK, dV of this lane's key: C[dim 16dt + 4g + r][key li]
-    if (keyw < T) {
-        float* dKh = dK + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)keyw * D;
-        float* dVh = dV + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)keyw * D;
+    // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1
 #pragma unroll
-        for (int dt = 0; dt < Tr::NDT; ++dt) {
-            const int d0 = 16 * dt + 4 * g;
-            if (Tr::DP == D || d0 < D) {
-                *(f32x4*)(dKh + d0) = dk[dt];
-                *(f32x4*)(dVh + d0) = dv[dt];
+    for (int r = 0; r < 4; ++r) {
+        const int key = kv0 + 16 * w + 4 * g + r;
+        if (key < T && (Tr::DP == D || li < D)) {
+            float* dKr = dK + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)key * D + Tr::NDT * li;
+            float* dVr = dV + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)key * D + Tr::NDT * li;
+            if constexpr (Tr::NDT % 4 == 0) {
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; dt += 4) {
+                    *(f32x4*)(dKr + dt) = f32x4{dk[dt][r], dk[dt + 1][r], dk[dt + 2][r], dk[dt + 3][r]};
+                    *(f32x4*)(dVr + dt) = f32x4{dv[dt][r], dv[dt + 1][r], dv[dt + 2][r], dv[dt + 3][r]};
+                }
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; ++dt) {
+                    dKr[dt] = dk[dt][r];
+                    dVr[dt] = dv[dt][r];
+                }
             }
         }
     }
