@@ -176,32 +176,59 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
         dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    for (int hh = 0; hh < G; ++hh) {
-        const int h = hk * G + hh;
+    // The (query head, query tile) pairs this block visits, in order; the next
+    // pair's Q, dO rows and row statistics are loaded into registers during the
+    // current pair's dQ phase and written to LDS at the top of the next step.
+    const int nqt = nqb - kb;
+    const int nsteps = G * nqt;
+    constexpr int PER = (Tr::TILE4 + Tr::NT - 1) / Tr::NT;
+    f32x4 xq[PER], xo[PER];
+    float xl = INFINITY, xd = 0.f;
+    auto prefetch = [&](int step) {
+        const int h = hk * G + step / nqt;
+        const int q0 = (kb + step % nqt) * Tr::BM;
         const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
-        const float* Qh = Q + hoff * D;
-        const float* dOh = dO + hoff * D;
-        float* dQh = dQ + hoff * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            const int row = idx / (D / 4), c4 = idx % (D / 4);
+            const int q = q0 + row;
+            xq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            xo[i] = xq[i];
+            if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && q < T) {
+                xq[i] = *(const f32x4*)(Q + (hoff + q) * D + 4 * c4);
+                xo[i] = *(const f32x4*)(dO + (hoff + q) * D + 4 * c4);
+            }
+        }
+        if (tid < Tr::BM) {
+            const int q = q0 + tid;
+            // a padding row gets LSE = +inf, so its probabilities are exactly 0
+            xl = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
+            xd = q < T ? Delta[hoff + q] : 0.f;
+        }
+    };
+    prefetch(0);
 
-        for (int qb = kb; qb < nqb; ++qb) {
+    for (int step = 0; step < nsteps; ++step) {
+        const int h = hk * G + step / nqt;
+        const int qb = kb + step % nqt;
+        const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
+        float* dQh = dQ + hoff * D;
+        {
             const int q0 = qb * Tr::BM;
             __syncthreads();  // the previous tile's LDS readers are done
-            for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
-                const int row = idx / (D / 4), c4 = idx % (D / 4);
-                const int q = q0 + row;
-                f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f}, y = x;
-                if (q < T) {
-                    x = *(const f32x4*)(Qh + (size_t)q * D + 4 * c4);
-                    y = *(const f32x4*)(dOh + (size_t)q * D + 4 * c4);
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int idx = tid + Tr::NT * i;
+                if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
+                    const int row = idx / (D / 4), c4 = idx % (D / 4);
+                    *(f32x4*)&Qs[row * Tr::LD + 4 * c4] = xq[i];
+                    *(f32x4*)&dOs[row * Tr::LD + 4 * c4] = xo[i];
                 }
-                *(f32x4*)&Qs[row * Tr::LD + 4 * c4] = x;
-                *(f32x4*)&dOs[row * Tr::LD + 4 * c4] = y;
             }
             if (tid < Tr::BM) {
-                const int q = q0 + tid;
-                // a padding row gets LSE = +inf, so its probabilities are exactly 0
-                lse2s[tid] = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
-                dls[tid] = q < T ? Delta[hoff + q] : 0.f;
+                lse2s[tid] = xl;
+                dls[tid] = xd;
             }
             __syncthreads();
 
@@ -279,6 +306,8 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
                     }
                 }
             }
+
+            if (step + 1 < nsteps) prefetch(step + 1);  // lands during the dQ phase
 
             // dS -> LDS as [query][key]
 #pragma unroll

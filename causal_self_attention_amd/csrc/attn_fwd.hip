@@ -15,8 +15,11 @@
 //   * each wave computes S^T = K Q^T on fp32 MFMA (16x16x4) with its Q rows held
 //     in registers, so a C tile has the query in the lane (i) and the keys in
 //     (g, r): the online-softmax statistics of a query stay in its four lanes;
-//   * P^T is then exactly the B operand of O^T += V^T P^T (keys are contracted
-//     in the permuted order (g, r), and V rows are read from LDS in that order);
+//   * P in that layout is exactly the A operand of O += P V (keys contracted in
+//     the permuted order (g, r)); the output dims are permuted so each lane reads
+//     its V values as one contiguous vector per key row;
+//   * the running max moves only when a score exceeds it by more than 2^8, so the
+//     output rescale (which needs a cross-lane shuffle in this layout) is rare;
 //   * only tiles with keys <= the block's last query are visited, and in the
 //     diagonal tile wave w skips the 16-key sub-tiles wholly above its rows;
 //   * blocks are ranked heaviest first (longest causal prefix) and dealt to the
@@ -48,6 +51,26 @@ __device__ __forceinline__ constexpr int frag_dim(int s, int g) {
     return 4 * W * (s / W) + W * g + (s % W);
 }
 
+constexpr float kFwdLazyRescale = 8.f;  // log2 headroom before the running max is moved
+
+template <int N>
+__device__ __forceinline__ void lds_vec(const float* p, float (&x)[N]) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const f32x4 v = *(const f32x4*)(p + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 * i + j] = v[j];
+        }
+    } else if constexpr (N == 2) {
+        const f32x2 v = *(const f32x2*)p;
+        x[0] = v[0];
+        x[1] = v[1];
+    } else {
+        x[0] = p[0];
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -73,7 +96,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const int q0 = qb * Tr::BM;
-    const int qrow = q0 + 16 * w + li;  // this lane's query row
+    const int qrow = q0 + 16 * w + li;  // this lane's query row (column of the S^T tiles)
 
     if constexpr (Tr::DP != D) {  // zero the padding columns of V once
         for (int idx = tid; idx < Tr::BN * (Tr::DP - D); idx += Tr::NT) {
@@ -98,11 +121,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         }
     }
 
+    // O accumulators as [query 16w + 4g + r][dim NDT*li + dt]
     f32x4 acc[Tr::NDT];
 #pragma unroll
     for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running row max, log2 units
-    float l_run = 0.f;        // this lane's part of the running row sum
+    float m_run = -INFINITY;  // running max of query qrow (log2 units), same in its four lanes
+    float l_run = 0.f;        // this lane's share of query qrow's running sum
 
     f32x4 kreg[Tr::PER], vreg[Tr::PER];
     auto gload = [&](int kv0) {
@@ -168,7 +192,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
             }
         }
 
-        // mask, scale to log2 units, row max over the 64 keys
+        // mask and scale to log2 units; this lane's max over its 16 keys of the tile
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -181,50 +205,67 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
                 mx = fmaxf(mx, x);
             }
         }
-        mx = rows4_max(mx);
-        const float m_new = fmaxf(m_run, mx);  // finite: key kv0 <= qrow is always visible
-        const float alpha = exp2_hw(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
+        // The running max moves only when a score exceeds it by more than 2^8 (and on
+        // the first tile); otherwise exponents stay <= 2^8 and no rescale is needed.
+        if (__ballot(mx > m_run + kFwdLazyRescale)) {  // wave-uniform
+            const float m_new = fmaxf(m_run, rows4_max(mx));  // finite: key kv0 <= qrow is visible
+            const float alpha = exp2_hw(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * g + r);  // alpha of query 16w + 4g + r
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt][r] *= ar;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = exp2_hw(st[t][r] - m_new);
+                const float p = exp2_hw(st[t][r] - m_run);
                 st[t][r] = p;
-                psum += p;
+                l_run += p;
             }
         }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] *= alpha;
 
-        // O^T += V^T P^T : k-step (t, r) pairs lane row g with key kv0 + 16t + 4g + r
+        // O += P V : P[query li][key 16t + 4g + r] is the A operand as it stands (k-step
+        // (t, r)); B = V rows, lane li taking dims NDT*li .. NDT*li+NDT-1 as one vector
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             if (t < nsub) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float* vp = &Vs[(16 * t + 4 * g + r) * Tr::LDV + li];
+                    float bv[Tr::NDT];
+                    lds_vec<Tr::NDT>(&Vs[(16 * t + 4 * g + r) * Tr::LDV + Tr::NDT * li], bv);
 #pragma unroll
-                    for (int dt = 0; dt < Tr::NDT; ++dt)
-                        acc[dt] = mfma16x16x4(vp[16 * dt], st[t][r], acc[dt]);
+                    for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = mfma16x16x4(st[t][r], bv[dt], acc[dt]);
                 }
             }
         }
     }
 
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-    const float l_tot = rows4_sum(l_run);
-    const float inv = 1.f / l_tot;
-    if (qrow < T) {
-        float* Oh = O + ((size_t)b * Hq + h) * (size_t)T * D + (size_t)qrow * D;
+    const float l_tot = rows4_sum(l_run);  // query qrow's sum, in lanes (*, li)
+    const float inv_own = 1.f / l_tot;
+    if (g == 0 && qrow < T) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_run + log2_hw(l_tot)) * kLn2;
+    float* Ob = O + ((size_t)b * Hq + h) * (size_t)T * D;
 #pragma unroll
-        for (int dt = 0; dt < Tr::NDT; ++dt) {
-            const int d0 = 16 * dt + 4 * g;
-            if (Tr::DP == D || d0 < D) *(f32x4*)(Oh + d0) = acc[dt] * inv;
+    for (int r = 0; r < 4; ++r) {
+        const float inv = __shfl(inv_own, 4 * g + r);  // 1/l of query 16w + 4g + r
+        const int q = q0 + 16 * w + 4 * g + r;
+        if (q < T && (Tr::DP == D || li < D)) {
+            float* dst = Ob + (size_t)q * D + Tr::NDT * li;
+            if constexpr (Tr::NDT % 4 == 0) {
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; dt += 4)
+                    *(f32x4*)(dst + dt) =
+                        f32x4{acc[dt][r] * inv, acc[dt + 1][r] * inv, acc[dt + 2][r] * inv, acc[dt + 3][r] * inv};
+            } else {
+#pragma unroll
+                for (int dt = 0; dt < Tr::NDT; ++dt) dst[dt] = acc[dt][r] * inv;
+            }
         }
-        if (g == 0) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_run + log2_hw(l_tot)) * kLn2;
     }
 }
 
