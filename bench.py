@@ -37,6 +37,10 @@ if ROOT not in sys.path:
 METRIC = "causal attn fwd+bwd TFLOP/s (fp32, % MFMA peak); paged-decode HBM GB/s"
 PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+# HBM bytes per attn_causal_bwd launch on the 1024-token workload, from FETCH_SIZE (x2.00)
+# and WRITE_SIZE (x1.00) counter passes; valid only for the kernel source they were taken on.
+BWD_TRAFFIC_BYTES = 155.9e6
+BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "e0d7220a05fa6446"
 CAUSAL = "mha_b4_h8_t1024_d64"
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"
 DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
@@ -54,6 +58,17 @@ def decode_bytes(d, Hq, Hkv, D):
     kv = sum(ctx) * Hkv * D * 4 * 2          # every K and V row once per KV head
     qo = 2 * S * Hq * D * 4                  # q in, o out
     return kv + qo + S * Hq * 4 + pages * 4 + S * 4  # + lse, used table entries, lengths
+
+
+def bwd_traffic():
+    """Counter-measured bytes per backward launch, or None if the kernel source changed."""
+    import hashlib
+    path = os.path.join(ROOT, "causal_self_attention_amd", "csrc", "attn_bwd.hip")
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return BWD_TRAFFIC_BYTES if digest.startswith(BWD_TRAFFIC_SOURCE_SHA256_PREFIX) else None
 
 
 def cpu_model():
@@ -76,6 +91,11 @@ def main():
     ap.add_argument("--gqa-iters", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-runs", type=int, default=3)
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="only fill, sum and copy a buffer of this many MiB (plain kernels of known "
+                         "traffic, to scale hardware byte counters) and exit")
+    ap.add_argument("--only", choices=["all", "bwd"], default="all",
+                    help="'bwd': run only the timed steps of forward + backward (for counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
@@ -89,6 +109,20 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+
+    if args.calibrate_copy_mb:
+        # known traffic: the fill writes n*4 bytes, each sum reads n*4 bytes, each copy
+        # reads and writes n*4 bytes
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        tot = torch.empty((), device=dev)
+        for _ in range(3):
+            torch.sum(src, dim=(0,), out=tot)
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_bytes": n * 4, "fill": 1, "sum": 3, "copy": 3}), flush=True)
+        return
 
     # ---- inputs and outputs, resident before timing ----
     cfg = si.CAUSAL_WORKLOADS[CAUSAL]
@@ -127,8 +161,9 @@ def main():
                              stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        kp, vp = pools[i % len(pools)]
-        attn.attn_paged_decode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
+        if args.only == "all":
+            kp, vp = pools[i % len(pools)]
+            attn.attn_paged_decode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -142,6 +177,9 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.only == "bwd":
+        print(json.dumps({"only": "bwd", "steps": args.steps}), flush=True)
+        return
     t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
     t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
     t_dec = [e[2].elapsed_time(e[3]) for e in evs]
@@ -202,7 +240,7 @@ def main():
             "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(bwd_tflops / PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": None,
+            "traffic": bwd_traffic(),
             "flops_per_launch": bwd_flops,
             "avg_launch_us": round(bwd_avg_s * 1e6, 2),
         },
