@@ -12,12 +12,20 @@
 // dS = P (dP - Delta):  dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Kernels, in stream order:
-//   1. attn_bwd_pre: Delta_i = <dO_i, O_i> into the workspace, and dQ = 0;
-//   2. attn_bwd_main: one work-group per 64-key block of one (batch, KV head);
+//   1. attn_bwd_pre: Delta_i = <dO_i, O_i> into the workspace, dQ = 0, and, when
+//      key blocks are shared between work-groups (below), dK = dV = 0 on the
+//      key blocks that may be shared;
+//   2. attn_bwd_main: the work of one (batch, KV head) is the list of steps
+//      (key block kb, query head, query tile >= kb) of all its key blocks.  For a
+//      long enough grid a work-group takes one whole key block, heaviest first.
+//      For a short grid the heaviest key block alone would set the kernel's
+//      length (key block 0 has the most steps), so the key blocks are ordered
+//      0, n-1, 1, n-2, ... -- every such pair has the same number of steps -- and
+//      each work-group takes half a pair.  A key block that is cut in two adds
+//      its dK, dV atomically onto zero; two addends onto zero give the same bits
+//      in either order, so the result stays deterministic.  Within a key block,
 //      wave w owns keys kv0+16w .. +15 and keeps their K, V fragments and dK, dV
-//      accumulators in registers while it walks every query tile at or below
-//      the diagonal, for each query head of the group.  Per query tile (64 rows,
-//      Q and dO staged in LDS):
+//      accumulators in registers.  Per step (64 query rows, Q and dO in LDS):
 //        S  = Q K^T, dP = dO V^T           (C tiles: key in the lane i)
 //        P, dS                             (elementwise, masked on the diagonal)
 //        dV += P^T dO,  dK += dS^T Q       (P and dS are the A operands as-is; the
@@ -37,11 +45,23 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const float* __restrict__ O,
                                                            const float* __restrict__ dO,
                                                            float* __restrict__ Delta,
-                                                           float* __restrict__ dQ, int64_t rows) {
+                                                           float* __restrict__ dQ, int64_t rows,
+                                                           float* __restrict__ dK, float* __restrict__ dV,
+                                                           int64_t T, int64_t nbkv, int64_t zrows) {
     constexpr int TPR = D / 4;  // threads per row, one float4 each
     constexpr int RPB = 256 / TPR;
     const int tid = threadIdx.x;
     const int part = tid % TPR;
+    const int64_t qblocks = (rows + RPB - 1) / RPB;
+    if ((int64_t)blockIdx.x >= qblocks) {  // trailing blocks: dK = dV = 0 on the first zrows keys of each head
+        const int64_t zr = ((int64_t)blockIdx.x - qblocks) * RPB + tid / TPR;
+        if (zr < nbkv * zrows) {
+            const int64_t row = (zr / zrows) * T + zr % zrows;
+            *(f32x4*)(dK + row * D + 4 * part) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *(f32x4*)(dV + row * D + 4 * part) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
     const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
     float x = 0.f;
     if (row < rows) {
@@ -67,8 +87,9 @@ struct BwdTraits {
     static constexpr int KSTEPS = D / 4;
     static constexpr int DP = D >= 16 ? D : 16;     // head dim padded to whole 16-column tiles
     static constexpr int NDT = DP / 16;             // C tiles over the head dim
-    static constexpr int LD = DP + 4;               // LDS row stride of Q, dO, K tiles
+    static constexpr int LD = DP + 4;               // LDS row stride of the Q, dO tiles
     static constexpr int LDS_ = BN + 4;             // LDS row stride of the dS tile
+    static constexpr int LDT = BN + 4;              // LDS row stride of the transposed K tile
     static constexpr int TILE4 = BM * D / 4;
 };
 
@@ -97,15 +118,15 @@ __device__ __forceinline__ void lds_row(const float* p, float (&x)[N]) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_bwd_main_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void attn_bwd_main_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
-    int nkb, int nbkv, int ncu, float scale, float c2 /* scale * log2(e) */) {
+    int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
-    __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LD];
+    __shared__ __attribute__((aligned(16))) float Kt[Tr::DP * Tr::LDT];  // K^T: [dim][key]
     __shared__ __attribute__((aligned(16))) float dSs[Tr::BM * Tr::LDS_];
     __shared__ __attribute__((aligned(16))) float lse2s[Tr::BM];
     __shared__ __attribute__((aligned(16))) float dls[Tr::BM];
@@ -116,261 +137,344 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
     const int li = lane & 15;
     const int g = lane >> 4;
 
-    const int rank = snake_rank(blockIdx.x, nkb * nbkv, ncu);
-    const int kb = rank / nbkv;  // key block 0 has the most query tiles: rank 0
-    const int bkv = rank % nbkv;
+    const int G = Hq / Hkv;
+    const int nqb = (T + Tr::BM - 1) / Tr::BM;  // == nkb (BM == BN)
+    // Key block kb has G * (nqb - kb) steps (query head, query tile >= kb).  In the
+    // paired order 0, nkb-1, 1, nkb-2, ... two neighbours hold G * (nkb + 1) steps
+    // together; position pi of that order is key block kb_at(pi), whose steps
+    // start at start_at(pi) in the concatenated list.
+    const int64_t pair_len = (int64_t)G * (nkb + 1);
+    auto kb_at = [&](int pi) { return (pi & 1) ? nkb - 1 - (pi >> 1) : (pi >> 1); };
+    auto start_at = [&](int pi) -> int64_t {
+        const int pr = pi >> 1;
+        return pr * pair_len + ((pi & 1) ? (int64_t)G * (nkb - pr) : 0);
+    };
+    int bkv, pi = 0, kb_fixed = 0;
+    int64_t s_begin, s_end;
+    if (runs == 0) {  // one work-group per key block, heaviest first
+        const int rank = blockIdx.x;
+        kb_fixed = rank / nbkv;
+        bkv = rank % nbkv;
+        s_begin = 0;
+        s_end = (int64_t)G * (nqb - kb_fixed);
+    } else {  // run `run` of `runs` (== nkb) equal runs: half a pair each
+        const int run = blockIdx.x / nbkv;
+        bkv = blockIdx.x % nbkv;
+        const int64_t total = (int64_t)G * nkb * (nkb + 1) / 2;
+        s_begin = (int64_t)run * total / runs;
+        s_end = (int64_t)(run + 1) * total / runs;
+        const int pr = (int)(s_begin / pair_len);
+        pi = 2 * pr + (s_begin - pr * pair_len >= (int64_t)G * (nkb - pr) ? 1 : 0);
+    }
     const int b = bkv / Hkv;
     const int hk = bkv % Hkv;
-    const int G = Hq / Hkv;
-    const int nqb = (T + Tr::BM - 1) / Tr::BM;
-    const int kv0 = kb * Tr::BN;
-    const int keyw = kv0 + 16 * w + li;  // this lane's key (column of the S / dP tiles)
-
     const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
+    float* dKh = dK + ((size_t)b * Hkv + hk) * (size_t)T * D;
+    float* dVh = dV + ((size_t)b * Hkv + hk) * (size_t)T * D;
 
-    if constexpr (Tr::DP != D) {  // padding columns of the Q, dO, K tiles stay zero
+    if constexpr (Tr::DP != D) {  // padding dims of the Q, dO, K tiles stay zero
         for (int idx = tid; idx < Tr::BM * (Tr::DP - D); idx += Tr::NT) {
             const int row = idx / (Tr::DP - D), col = D + idx % (Tr::DP - D);
             Qs[row * Tr::LD + col] = 0.f;
             dOs[row * Tr::LD + col] = 0.f;
-            Ks[row * Tr::LD + col] = 0.f;
+            Kt[col * Tr::LDT + row] = 0.f;
         }
     }
 
-    // K, V fragments of this lane's key: slot s holds [keyw][frag_dim_b(s, g)]
-    float kf[Tr::KSTEPS], vf[Tr::KSTEPS];
-#pragma unroll
-    for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
-        const int d0 = 4 * Tr::W * u + Tr::W * g;
-        if constexpr (Tr::W == 4) {
-            f32x4 x = keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-            f32x4 y = keyw < T ? *(const f32x4*)(Vh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kf[4 * u + j] = x[j];
-                vf[4 * u + j] = y[j];
-            }
-        } else {
-            f32x2 x = keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
-            f32x2 y = keyw < T ? *(const f32x2*)(Vh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
-            kf[2 * u] = x[0];
-            kf[2 * u + 1] = x[1];
-            vf[2 * u] = y[0];
-            vf[2 * u + 1] = y[1];
-        }
-    }
-    // the key block's K tile in LDS (B operand of dQ = dS K)
-    for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
-        const int row = idx / (D / 4), c4 = idx % (D / 4);
-        const int key = kv0 + row;
-        *(f32x4*)&Ks[row * Tr::LD + 4 * c4] =
-            key < T ? *(const f32x4*)(Kh + (size_t)key * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    if (s_begin >= s_end) return;
 
-    // dK, dV accumulators as [key 4g + r][dim NDT*li + dt] (this wave's 16 keys)
-    f32x4 dk[Tr::NDT], dv[Tr::NDT];
-#pragma unroll
-    for (int dt = 0; dt < Tr::NDT; ++dt) {
-        dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    // The (query head, query tile) pairs this block visits, in order; the next
-    // pair's Q, dO rows and row statistics are loaded into registers during the
-    // current pair's dQ phase and written to LDS at the top of the next step.
-    const int nqt = nqb - kb;
-    const int nsteps = G * nqt;
     constexpr int PER = (Tr::TILE4 + Tr::NT - 1) / Tr::NT;
     f32x4 xq[PER], xo[PER];
     float xl = INFINITY, xd = 0.f;
-    auto prefetch = [&](int step) {
-        const int h = hk * G + step / nqt;
-        const int q0 = (kb + step % nqt) * Tr::BM;
-        const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
+
+    // One segment per key block that the run touches (at most two; wave-uniform).
+    for (int64_t s = s_begin; s < s_end; ++pi) {
+        const int kb = runs ? kb_at(pi) : kb_fixed;
+        const int64_t kb_first = runs ? start_at(pi) : 0;
+        const int64_t kb_end = kb_first + (int64_t)G * (nqb - kb);
+        const int64_t seg_end = s_end < kb_end ? s_end : kb_end;
+        const bool whole = (s == kb_first && seg_end == kb_end);  // no other run shares this key block
+        const int j0 = (int)(s - kb_first), j1 = (int)(seg_end - kb_first);
+        s = seg_end;
+        const int nqt = nqb - kb;
+        const int kv0 = kb * Tr::BN;
+        const int keyw = kv0 + 16 * w + li;  // this lane's key (column of the S / dP tiles)
+
+        __syncthreads();  // the previous segment's readers of Kt are done
+
+        // K, V fragments of this lane's key: slot s holds [keyw][frag_dim_b(s, g)]
+        float kf[Tr::KSTEPS], vf[Tr::KSTEPS];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int idx = tid + Tr::NT * i;
-            const int row = idx / (D / 4), c4 = idx % (D / 4);
-            const int q = q0 + row;
-            xq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-            xo[i] = xq[i];
-            if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && q < T) {
-                xq[i] = *(const f32x4*)(Q + (hoff + q) * D + 4 * c4);
-                xo[i] = *(const f32x4*)(dO + (hoff + q) * D + 4 * c4);
+        for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+            const int d0 = 4 * Tr::W * u + Tr::W * g;
+            if constexpr (Tr::W == 4) {
+                f32x4 x = keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 y = keyw < T ? *(const f32x4*)(Vh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    kf[4 * u + j] = x[j];
+                    vf[4 * u + j] = y[j];
+                }
+            } else {
+                f32x2 x = keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+                f32x2 y = keyw < T ? *(const f32x2*)(Vh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+                kf[2 * u] = x[0];
+                kf[2 * u + 1] = x[1];
+                vf[2 * u] = y[0];
+                vf[2 * u + 1] = y[1];
             }
         }
-        if (tid < Tr::BM) {
-            const int q = q0 + tid;
-            // a padding row gets LSE = +inf, so its probabilities are exactly 0
-            xl = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
-            xd = q < T ? Delta[hoff + q] : 0.f;
+        // the key block's K tile in LDS, transposed (B operand of dQ = dS K: four
+        // consecutive keys of one dim are one vector read)
+        for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
+            const int row = idx / (D / 4), c4 = idx % (D / 4);
+            const int key = kv0 + row;
+            const f32x4 x = key < T ? *(const f32x4*)(Kh + (size_t)key * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) Kt[(4 * c4 + c) * Tr::LDT + row] = x[c];
         }
-    };
-    prefetch(0);
 
-    for (int step = 0; step < nsteps; ++step) {
-        const int h = hk * G + step / nqt;
-        const int qb = kb + step % nqt;
-        const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
-        float* dQh = dQ + hoff * D;
-        {
-            const int q0 = qb * Tr::BM;
-            __syncthreads();  // the previous tile's LDS readers are done
+        // dK, dV accumulators as [key 4g + r][dim NDT*li + dt] (this wave's 16 keys)
+        f32x4 dk[Tr::NDT], dv[Tr::NDT];
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) {
+            dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+
+        // Step j of the key block is query head hk*G + j / nqt, query tile kb + j % nqt.
+        // The next step's Q, dO rows and row statistics are loaded into registers
+        // during the current step's dQ phase and written to LDS at the top of the next.
+        auto prefetch = [&](int step) {
+            const int h = hk * G + step / nqt;
+            const int q0 = (kb + step % nqt) * Tr::BM;
+            const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
 #pragma unroll
             for (int i = 0; i < PER; ++i) {
                 const int idx = tid + Tr::NT * i;
-                if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
-                    const int row = idx / (D / 4), c4 = idx % (D / 4);
-                    *(f32x4*)&Qs[row * Tr::LD + 4 * c4] = xq[i];
-                    *(f32x4*)&dOs[row * Tr::LD + 4 * c4] = xo[i];
+                const int row = idx / (D / 4), c4 = idx % (D / 4);
+                const int q = q0 + row;
+                xq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+                xo[i] = xq[i];
+                if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && q < T) {
+                    xq[i] = *(const f32x4*)(Q + (hoff + q) * D + 4 * c4);
+                    xo[i] = *(const f32x4*)(dO + (hoff + q) * D + 4 * c4);
                 }
             }
             if (tid < Tr::BM) {
-                lse2s[tid] = xl;
-                dls[tid] = xd;
+                const int q = q0 + tid;
+                // a padding row gets LSE = +inf, so its probabilities are exactly 0
+                xl = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
+                xd = q < T ? Delta[hoff + q] : 0.f;
             }
-            __syncthreads();
+        };
+        prefetch(j0);
 
-            // Every sub-tile is computed, also on the diagonal where some lie wholly above
-            // this wave's keys: their probabilities are zeroed by the causal select below.
-            // Skipping them would put branches around accumulating MFMAs, and the compiler
-            // then copies the accumulators at every join, which costs more than it saves.
-            const bool diag = (qb == kb);
+        for (int step = j0; step < j1; ++step) {
+            const int h = hk * G + step / nqt;
+            const int qb = kb + step % nqt;
+            const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
+            float* dQh = dQ + hoff * D;
+            {
+                const int q0 = qb * Tr::BM;
+                __syncthreads();  // the previous tile's LDS readers are done
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int idx = tid + Tr::NT * i;
+                    if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
+                        const int row = idx / (D / 4), c4 = idx % (D / 4);
+                        *(f32x4*)&Qs[row * Tr::LD + 4 * c4] = xq[i];
+                        *(f32x4*)&dOs[row * Tr::LD + 4 * c4] = xo[i];
+                    }
+                }
+                if (tid < Tr::BM) {
+                    lse2s[tid] = xl;
+                    dls[tid] = xd;
+                }
+                __syncthreads();
 
-            // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li]
-            f32x4 sa[4], pa[4];
+                // Every sub-tile is computed, also on the diagonal where some lie wholly above
+                // this wave's keys: their probabilities are zeroed by the causal select below.
+                // Skipping them would put branches around accumulating MFMAs, and the compiler
+                // then copies the accumulators at every join, which costs more than it saves.
+                const bool diag = (qb == kb);
+
+                // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li]
+                f32x4 sa[4], pa[4];
 #pragma unroll
-            for (int qs = 0; qs < 4; ++qs) {
-                sa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
-                {
+                for (int qs = 0; qs < 4; ++qs) {
+                    sa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    {
 #pragma unroll
-                    for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
-                        const int off = (16 * qs + li) * Tr::LD + 4 * Tr::W * u + Tr::W * g;
-                        if constexpr (Tr::W == 4) {
-                            const f32x4 a = *(const f32x4*)&Qs[off];
-                            const f32x4 c = *(const f32x4*)&dOs[off];
+                        for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+                            const int off = (16 * qs + li) * Tr::LD + 4 * Tr::W * u + Tr::W * g;
+                            if constexpr (Tr::W == 4) {
+                                const f32x4 a = *(const f32x4*)&Qs[off];
+                                const f32x4 c = *(const f32x4*)&dOs[off];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                sa[qs] = mfma16x16x4(a[j], kf[4 * u + j], sa[qs]);
-                                pa[qs] = mfma16x16x4(c[j], vf[4 * u + j], pa[qs]);
-                            }
-                        } else {
-                            const f32x2 a = *(const f32x2*)&Qs[off];
-                            const f32x2 c = *(const f32x2*)&dOs[off];
+                                for (int j = 0; j < 4; ++j) {
+                                    sa[qs] = mfma16x16x4(a[j], kf[4 * u + j], sa[qs]);
+                                    pa[qs] = mfma16x16x4(c[j], vf[4 * u + j], pa[qs]);
+                                }
+                            } else {
+                                const f32x2 a = *(const f32x2*)&Qs[off];
+                                const f32x2 c = *(const f32x2*)&dOs[off];
 #pragma unroll
-                            for (int j = 0; j < 2; ++j) {
-                                sa[qs] = mfma16x16x4(a[j], kf[2 * u + j], sa[qs]);
-                                pa[qs] = mfma16x16x4(c[j], vf[2 * u + j], pa[qs]);
+                                for (int j = 0; j < 2; ++j) {
+                                    sa[qs] = mfma16x16x4(a[j], kf[2 * u + j], sa[qs]);
+                                    pa[qs] = mfma16x16x4(c[j], vf[2 * u + j], pa[qs]);
+                                }
                             }
                         }
                     }
                 }
-            }
 
-            // P = exp(s - LSE) (0 where masked), dS = scale * P * (dP - Delta).  Row
-            // statistics come in as one vector per sub-tile; the mask is a select.
+                // P = exp(s - LSE) (0 where masked), dS = scale * P * (dP - Delta).  Row
+                // statistics come in as one vector per sub-tile; the mask is a select.
 #pragma unroll
-            for (int qs = 0; qs < 4; ++qs) {
-                const f32x4 l4 = *(const f32x4*)&lse2s[16 * qs + 4 * g];
-                const f32x4 d4 = *(const f32x4*)&dls[16 * qs + 4 * g];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int qr = 16 * qs + 4 * g + r;  // row within the tile
-                    float p = exp2_hw(sa[qs][r] * c2 - l4[r]);
-                    p = (diag && 16 * w + li > qr) ? 0.f : p;
-                    const float ds = scale * p * (pa[qs][r] - d4[r]);
-                    sa[qs][r] = p;
-                    pa[qs][r] = ds;
-                }
-            }
-
-            // dV += P^T dO and dK += dS^T Q with P, dS as the A operands straight from their
-            // accumulators (k-step (qs, r) pairs lane row g with query 16qs + 4g + r) and the
-            // dO / Q rows as B operands, lane li taking dims NDT*li .. NDT*li+NDT-1
-#pragma unroll
-            for (int qs = 0; qs < 4; ++qs) {
-                {
+                for (int qs = 0; qs < 4; ++qs) {
+                    const f32x4 l4 = *(const f32x4*)&lse2s[16 * qs + 4 * g];
+                    const f32x4 d4 = *(const f32x4*)&dls[16 * qs + 4 * g];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int row = (16 * qs + 4 * g + r) * Tr::LD + Tr::NDT * li;
-                        float bo[Tr::NDT], bq[Tr::NDT];
-                        lds_row<Tr::NDT>(&dOs[row], bo);
-                        lds_row<Tr::NDT>(&Qs[row], bq);
+                        const int qr = 16 * qs + 4 * g + r;  // row within the tile
+                        float p = exp2_hw(sa[qs][r] * c2 - l4[r]);
+                        p = (diag && 16 * w + li > qr) ? 0.f : p;
+                        const float ds = scale * p * (pa[qs][r] - d4[r]);
+                        sa[qs][r] = p;
+                        pa[qs][r] = ds;
+                    }
+                }
+
+                // dV += P^T dO and dK += dS^T Q with P, dS as the A operands straight from their
+                // accumulators (k-step (qs, r) pairs lane row g with query 16qs + 4g + r) and the
+                // dO / Q rows as B operands, lane li taking dims NDT*li .. NDT*li+NDT-1
 #pragma unroll
-                        for (int dt = 0; dt < Tr::NDT; ++dt) {
-                            dv[dt] = mfma16x16x4(sa[qs][r], bo[dt], dv[dt]);
-                            dk[dt] = mfma16x16x4(pa[qs][r], bq[dt], dk[dt]);
+                for (int qs = 0; qs < 4; ++qs) {
+                    {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = (16 * qs + 4 * g + r) * Tr::LD + Tr::NDT * li;
+                            float bo[Tr::NDT], bq[Tr::NDT];
+                            lds_row<Tr::NDT>(&dOs[row], bo);
+                            lds_row<Tr::NDT>(&Qs[row], bq);
+#pragma unroll
+                            for (int dt = 0; dt < Tr::NDT; ++dt) {
+                                dv[dt] = mfma16x16x4(sa[qs][r], bo[dt], dv[dt]);
+                                dk[dt] = mfma16x16x4(pa[qs][r], bq[dt], dk[dt]);
+                            }
                         }
                     }
                 }
-            }
 
-            if (step + 1 < nsteps) prefetch(step + 1);  // lands during the dQ phase
+                if (step + 1 < j1) prefetch(step + 1);  // lands during the dQ phase
 
-            // dS -> LDS as [query][key]
+                // dS -> LDS as [query][key]
 #pragma unroll
-            for (int qs = 0; qs < 4; ++qs)
+                for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dSs[(16 * qs + 4 * g + r) * Tr::LDS_ + 16 * w + li] = pa[qs][r];
-            __syncthreads();
+                    for (int r = 0; r < 4; ++r) dSs[(16 * qs + 4 * g + r) * Tr::LDS_ + 16 * w + li] = pa[qs][r];
+                __syncthreads();
 
-            // dQ rows 16w .. 16w+15 of the tile: C[query 16w + 4g + r][dim 16dt + li]
-            // k-step (u, j) pairs lane row g with key 16u + 4g + j
-            f32x4 qa[Tr::NDT];
+                // dQ rows 16w .. 16w+15 of the tile: C[query 16w + 4g + r][dim 16dt + li]
+                // k-step (u, j) pairs lane row g with key 16u + 4g + j
+                f32x4 qa[Tr::NDT];
 #pragma unroll
-            for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                {
-                    const f32x4 a = *(const f32x4*)&dSs[(16 * w + li) * Tr::LDS_ + 16 * u + 4 * g];
+                for (int u = 0; u < 4; ++u) {
+                    {
+                        const f32x4 a = *(const f32x4*)&dSs[(16 * w + li) * Tr::LDS_ + 16 * u + 4 * g];
+                        f32x4 kb[Tr::NDT];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float* kp = &Ks[(16 * u + 4 * g + j) * Tr::LD + li];
+                        for (int dt = 0; dt < Tr::NDT; ++dt)
+                            kb[dt] = *(const f32x4*)&Kt[(16 * dt + li) * Tr::LDT + 16 * u + 4 * g];
 #pragma unroll
-                        for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = mfma16x16x4(a[j], kp[16 * dt], qa[dt]);
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = mfma16x16x4(a[j], kb[dt][j], qa[dt]);
                     }
                 }
-            }
-            if (q0 + Tr::BM <= T && Tr::DP == D) {  // full tile: no per-element checks
+                if constexpr (Tr::NDT % 4 == 0) {
+                    // Transpose each 4x4 block (lane row g) x (dim tile dt) with the row-swap
+                    // permutes so that one atomic instruction covers 64 consecutive dims of
+                    // one query row: afterwards register x of lane (g, li) holds
+                    // dQ[query 16w + 4x + r][dim 64c + 16g + li].
 #pragma unroll
-                for (int dt = 0; dt < Tr::NDT; ++dt)
+                    for (int c = 0; c < Tr::NDT / 4; ++c) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        unsafeAtomicAdd(dQh + (size_t)(q0 + 16 * w + 4 * g + r) * D + 16 * dt + li, qa[dt][r]);
-            } else {
+                        for (int r = 0; r < 4; ++r) {
+                            float m[4] = {qa[4 * c][r], qa[4 * c + 1][r], qa[4 * c + 2][r], qa[4 * c + 3][r]};
+                            swap_rows32(m[0], m[2]);
+                            swap_rows32(m[1], m[3]);
+                            swap_rows16(m[0], m[1]);
+                            swap_rows16(m[2], m[3]);
 #pragma unroll
-                for (int dt = 0; dt < Tr::NDT; ++dt) {
-                    const int d = 16 * dt + li;
+                            for (int x = 0; x < 4; ++x) {
+                                const int q = q0 + 16 * w + 4 * x + r;
+                                if (q < T) unsafeAtomicAdd(dQh + (size_t)q * D + 64 * c + lane, m[x]);
+                            }
+                        }
+                    }
+                } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int q = q0 + 16 * w + 4 * g + r;
-                        if (q < T && (Tr::DP == D || d < D)) unsafeAtomicAdd(dQh + (size_t)q * D + d, qa[dt][r]);
+                    for (int dt = 0; dt < Tr::NDT; ++dt) {
+                        const int d = 16 * dt + li;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int q = q0 + 16 * w + 4 * g + r;
+                            if (q < T && (Tr::DP == D || d < D)) unsafeAtomicAdd(dQh + (size_t)q * D + d, qa[dt][r]);
+                        }
                     }
                 }
             }
         }
-    }
 
-    // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1
+        // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1.
+        if (whole) {  // no other run shares this key block: plain stores
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int key = kv0 + 16 * w + 4 * g + r;
-        if (key < T && (Tr::DP == D || li < D)) {
-            float* dKr = dK + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)key * D + Tr::NDT * li;
-            float* dVr = dV + ((size_t)b * Hkv + hk) * (size_t)T * D + (size_t)key * D + Tr::NDT * li;
-            if constexpr (Tr::NDT % 4 == 0) {
+            for (int r = 0; r < 4; ++r) {
+                const int key = kv0 + 16 * w + 4 * g + r;
+                if (key < T && (Tr::DP == D || li < D)) {
+                    float* dKr = dKh + (size_t)key * D + Tr::NDT * li;
+                    float* dVr = dVh + (size_t)key * D + Tr::NDT * li;
+                    if constexpr (Tr::NDT % 4 == 0) {
 #pragma unroll
-                for (int dt = 0; dt < Tr::NDT; dt += 4) {
-                    *(f32x4*)(dKr + dt) = f32x4{dk[dt][r], dk[dt + 1][r], dk[dt + 2][r], dk[dt + 3][r]};
-                    *(f32x4*)(dVr + dt) = f32x4{dv[dt][r], dv[dt + 1][r], dv[dt + 2][r], dv[dt + 3][r]};
+                        for (int dt = 0; dt < Tr::NDT; dt += 4) {
+                            *(f32x4*)(dKr + dt) = f32x4{dk[dt][r], dk[dt + 1][r], dk[dt + 2][r], dk[dt + 3][r]};
+                            *(f32x4*)(dVr + dt) = f32x4{dv[dt][r], dv[dt + 1][r], dv[dt + 2][r], dv[dt + 3][r]};
+                        }
+                    } else {
+#pragma unroll
+                        for (int dt = 0; dt < Tr::NDT; ++dt) {
+                            dKr[dt] = dk[dt][r];
+                            dVr[dt] = dv[dt][r];
+                        }
+                    }
                 }
-            } else {
+            }
+        } else {
+            // Shared with another run: add onto the zeroed outputs.  The block goes
+            // through LDS (the Q and dO tiles are free now) so that each atomic
+            // instruction covers whole rows.
+            __syncthreads();  // the last step's readers of Qs, dOs are done
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = (16 * w + 4 * g + r) * Tr::LD + Tr::NDT * li;
 #pragma unroll
                 for (int dt = 0; dt < Tr::NDT; ++dt) {
-                    dKr[dt] = dk[dt][r];
-                    dVr[dt] = dv[dt][r];
+                    Qs[row + dt] = dk[dt][r];
+                    dOs[row + dt] = dv[dt][r];
+                }
+            }
+            __syncthreads();
+            for (int idx = tid; idx < Tr::BN * D; idx += Tr::NT) {
+                const int kr = idx / D, d = idx % D;
+                if (kv0 + kr < T) {
+                    unsafeAtomicAdd(dKh + (size_t)(kv0 + kr) * D + d, Qs[kr * Tr::LD + d]);
+                    unsafeAtomicAdd(dVh + (size_t)(kv0 + kr) * D + d, dOs[kr * Tr::LD + d]);
                 }
             }
         }
@@ -380,19 +484,27 @@ __global__ __launch_bounds__(256) void attn_bwd_main_kernel(
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     using Tr = BwdTraits<D>;
-    const int64_t rows = a.B * a.Hq * a.T;
-    constexpr int RPB = 256 / (D / 4);
-    hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                       stream, a.o, a.dout, a.delta, a.dq, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int nkb = (int)((a.T + Tr::BN - 1) / Tr::BN);
     const int nbkv = (int)(a.B * a.Hkv);
-    const int n = nkb * nbkv;
-    const int ncu = n <= 2 * a.cu_count ? a.cu_count : n;  // snake only when all groups are resident
-    hipLaunchKernelGGL(attn_bwd_main_kernel<D>, dim3((unsigned)(nkb * nbkv)), dim3(Tr::NT), 0, stream, a.q,
-                       a.k, a.v, a.dout, a.lse, a.delta, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
-                       nbkv, ncu, a.scale, a.scale * kLog2e);
+    const int n = nkb * nbkv;  // work-groups with one key block each
+    // Two work-groups fit on a CU.  When all key blocks are resident at once, the
+    // heaviest one alone would set the kernel's length: take half pairs instead.
+    const int runs = n <= 2 * a.cu_count ? nkb : 0;
+    const int64_t rows = a.B * a.Hq * a.T;
+    // Only the first key block of a pair can be cut in two (the cut falls inside
+    // it), so only key blocks 0 .. nkb/2 - 1 are added atomically and need zeroing.
+    int64_t zrows = runs > 0 ? (int64_t)(nkb / 2) * Tr::BN : 0;
+    if (zrows > a.T) zrows = a.T;
+    constexpr int RPB = 256 / (D / 4);
+    const int64_t pre_blocks = (rows + RPB - 1) / RPB + (nbkv * zrows + RPB - 1) / RPB;
+    hipLaunchKernelGGL(attn_bwd_pre_kernel<D>, dim3((unsigned)pre_blocks), dim3(256), 0, stream, a.o, a.dout,
+                       a.delta, a.dq, rows, a.dk, a.dv, a.T, (int64_t)nbkv, zrows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned grid = runs > 0 ? (unsigned)(runs * nbkv) : (unsigned)n;
+    hipLaunchKernelGGL(attn_bwd_main_kernel<D>, dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v, a.dout,
+                       a.lse, a.delta, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb, nbkv, runs,
+                       a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 

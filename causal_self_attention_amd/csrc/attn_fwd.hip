@@ -8,8 +8,11 @@
 // maxima and exponential sums -- here folded into one log-sum-exp per row).
 //
 // Work decomposition (MI355X-first; the pages' tile-8 kernels are not reused):
-//   * one work-group = 4 waves = 64 query rows of one (batch, query head);
-//     wave w owns rows q0+16w .. q0+16w+15;
+//   * one work-group = 8 waves = 64 query rows of one (batch, query head); wave w
+//     owns rows q0+16(w%4) .. +15 and the key half w/4 of every 64-key tile, so
+//     the heaviest (longest-prefix) blocks have half the serial work per wave;
+//     the two halves keep separate softmax statistics and are merged through
+//     LDS at the end;
 //   * K/V tiles of 64 keys are staged in LDS through registers (the next tile's
 //     global loads are in flight while the current tile is multiplied);
 //   * each wave computes S^T = K Q^T on fp32 MFMA (16x16x4) with its Q rows held
@@ -21,11 +24,13 @@
 //   * the running max moves only when a score exceeds it by more than 2^8, so the
 //     output rescale (which needs a cross-lane shuffle in this layout) is rare;
 //   * only tiles with keys <= the block's last query are visited, and in the
-//     diagonal tile wave w skips the 16-key sub-tiles wholly above its rows;
+//     diagonal tile a wave skips the 16-key sub-tiles wholly above its rows;
 //   * blocks are ranked heaviest first (longest causal prefix) and dealt to the
 //     CUs in snake order (see snake_rank), which balances the triangular work.
 #include "attn_launch.h"
 #include "device_common.h"
+
+#include <float.h>
 
 namespace attn {
 
@@ -33,15 +38,19 @@ template <int D>
 struct FwdTraits {
     static constexpr int BM = 64;                     // query rows per work-group
     static constexpr int BN = 64;                     // keys per K/V tile
-    static constexpr int NT = 256;                    // threads per work-group
+    static constexpr int NT = 512;                    // threads per work-group (8 waves)
     static constexpr int W = D >= 16 ? 4 : 2;         // contiguous head-dim values per lane in a fragment
     static constexpr int KSTEPS = D / 4;              // MFMA k-steps over the head dim
-    static constexpr int DP = D >= 16 ? D : 16;       // head dim padded to whole 16-row O^T tiles
-    static constexpr int NDT = DP / 16;               // O^T tiles per wave
+    static constexpr int DP = D >= 16 ? D : 16;       // head dim padded to whole 16-column O tiles
+    static constexpr int NDT = DP / 16;               // O tiles per wave
     static constexpr int LDK = D + 4;                 // LDS row stride of the K tile (floats)
     static constexpr int LDV = DP + 4;                // LDS row stride of the V tile (floats)
     static constexpr int TILE4 = BN * D / 4;          // float4 loads per K (or V) tile
     static constexpr int PER = (TILE4 + NT - 1) / NT; // float4 loads per thread per tile
+    static constexpr int KS_FLOATS = BN * LDK;
+    static constexpr int SMEM_FLOATS = BN * LDK + BN * LDV;
+    static constexpr int MERGE_REGS = 4 * NDT + 2;    // per lane: O accumulators, max, sum
+    static_assert(4 * MERGE_REGS * 64 <= SMEM_FLOATS, "merge buffer must fit in the K/V tiles");
 };
 
 // Head-dim index of fragment slot s held by lane row g: groups of W contiguous
@@ -72,17 +81,20 @@ __device__ __forceinline__ void lds_vec(const float* p, float (&x)[N]) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(
+__global__ __launch_bounds__(512) void attn_fwd_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int T, int nqb, int nbh, int ncu,
     float c2 /* scale * log2(e) */) {
     using Tr = FwdTraits<D>;
-    __shared__ __attribute__((aligned(16))) float Ks[Tr::BN * Tr::LDK];
-    __shared__ __attribute__((aligned(16))) float Vs[Tr::BN * Tr::LDV];
+    __shared__ __attribute__((aligned(16))) float smem[Tr::SMEM_FLOATS];
+    float* Ks = smem;
+    float* Vs = smem + Tr::KS_FLOATS;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = wave_uniform(tid >> 6);
+    const int rw = w & 3;   // row group: rows q0 + 16rw .. +15
+    const int kh = w >> 2;  // key half: sub-tiles 2kh, 2kh+1 of every tile
     const int li = lane & 15;
     const int g = lane >> 4;
 
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
     const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const int q0 = qb * Tr::BM;
-    const int qrow = q0 + 16 * w + li;  // this lane's query row (column of the S^T tiles)
+    const int qrow = q0 + 16 * rw + li;  // this lane's query row (column of the S^T tiles)
 
     if constexpr (Tr::DP != D) {  // zero the padding columns of V once
         for (int idx = tid; idx < Tr::BN * (Tr::DP - D); idx += Tr::NT) {
@@ -121,12 +133,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         }
     }
 
-    // O accumulators as [query 16w + 4g + r][dim NDT*li + dt]
+    // O accumulators as [query 16rw + 4g + r][dim NDT*li + dt]
     f32x4 acc[Tr::NDT];
 #pragma unroll
     for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;  // running max of query qrow (log2 units), same in its four lanes
-    float l_run = 0.f;        // this lane's share of query qrow's running sum
+    // Running max of query qrow over this key half (log2 units, same in its four
+    // lanes).  It starts at the lowest finite value rather than -inf so that a
+    // half that sees no key yet gives exp2(-inf - m) = 0, never NaN.
+    float m_run = -FLT_MAX;
+    float l_run = 0.f;  // this lane's share of the half's running sum for query qrow
 
     f32x4 kreg[Tr::PER], vreg[Tr::PER];
     auto gload = [&](int kv0) {
@@ -168,13 +183,15 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
 
         const int kv0 = j * Tr::BN;
         const bool diag = (j == qb);
-        const int nsub = diag ? w + 1 : 4;  // 16-key sub-tiles with any key <= this wave's rows
+        const int nsub = diag ? rw + 1 : 4;  // 16-key sub-tiles with any key <= this wave's rows
 
-        // S^T = K Q^T : st[t] holds S^T[key = kv0 + 16t + 4g + r][query = qrow]
-        f32x4 st[4];
+        // S^T = K Q^T over this wave's key half: st[tt] holds
+        // S^T[key = kv0 + 16(2kh + tt) + 4g + r][query = qrow]
+        f32x4 st[2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * kh + tt;
+            st[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (t < nsub) {
 #pragma unroll
                 for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
@@ -182,49 +199,50 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
                     if constexpr (Tr::W == 4) {
                         const f32x4 a = *(const f32x4*)kp;
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) st[t] = mfma16x16x4(a[jj], qf[4 * u + jj], st[t]);
+                        for (int jj = 0; jj < 4; ++jj) st[tt] = mfma16x16x4(a[jj], qf[4 * u + jj], st[tt]);
                     } else {
                         const f32x2 a = *(const f32x2*)kp;
-                        st[t] = mfma16x16x4(a[0], qf[2 * u], st[t]);
-                        st[t] = mfma16x16x4(a[1], qf[2 * u + 1], st[t]);
+                        st[tt] = mfma16x16x4(a[0], qf[2 * u], st[tt]);
+                        st[tt] = mfma16x16x4(a[1], qf[2 * u + 1], st[tt]);
                     }
                 }
             }
         }
 
-        // mask and scale to log2 units; this lane's max over its 16 keys of the tile
+        // mask and scale to log2 units; this lane's max over its 8 keys of the tile
         float mx = -INFINITY;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * kh + tt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = kv0 + 16 * t + 4 * g + r;
-                float x = st[t][r] * c2;
+                float x = st[tt][r] * c2;
                 if (t >= nsub || (diag && key > qrow)) x = -INFINITY;
-                st[t][r] = x;
+                st[tt][r] = x;
                 mx = fmaxf(mx, x);
             }
         }
         // The running max moves only when a score exceeds it by more than 2^8 (and on
-        // the first tile); otherwise exponents stay <= 2^8 and no rescale is needed.
+        // the first visible key); otherwise exponents stay <= 2^8 and no rescale is needed.
         if (__ballot(mx > m_run + kFwdLazyRescale)) {  // wave-uniform
-            const float m_new = fmaxf(m_run, rows4_max(mx));  // finite: key kv0 <= qrow is visible
+            const float m_new = fmaxf(m_run, rows4_max(mx));
             const float alpha = exp2_hw(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * g + r);  // alpha of query 16w + 4g + r
+                const float ar = __shfl(alpha, 4 * g + r);  // alpha of query 16rw + 4g + r
 #pragma unroll
                 for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt][r] *= ar;
             }
         }
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = exp2_hw(st[t][r] - m_run);
-                st[t][r] = p;
+                const float p = exp2_hw(st[tt][r] - m_run);
+                st[tt][r] = p;
                 l_run += p;
             }
         }
@@ -232,38 +250,63 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(
         // O += P V : P[query li][key 16t + 4g + r] is the A operand as it stands (k-step
         // (t, r)); B = V rows, lane li taking dims NDT*li .. NDT*li+NDT-1 as one vector
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 2 * kh + tt;
             if (t < nsub) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     float bv[Tr::NDT];
                     lds_vec<Tr::NDT>(&Vs[(16 * t + 4 * g + r) * Tr::LDV + Tr::NDT * li], bv);
 #pragma unroll
-                    for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = mfma16x16x4(st[t][r], bv[dt], acc[dt]);
+                    for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = mfma16x16x4(st[tt][r], bv[dt], acc[dt]);
                 }
             }
         }
     }
 
-    // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
-    const float l_tot = rows4_sum(l_run);  // query qrow's sum, in lanes (*, li)
+    // Merge the two key halves.  Half 1 hands its accumulators, max and sum to the
+    // half-0 wave of the same rows through LDS, in the lanes' own register layout.
+    const float l_half = rows4_sum(l_run);  // query qrow's sum over this half, in lanes (*, li)
+    float* mbuf = smem + rw * Tr::MERGE_REGS * 64 + lane;
+    __syncthreads();  // the last tile's readers are done with the K/V buffers
+    if (kh == 1) {
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mbuf[(4 * dt + r) * 64] = acc[dt][r];
+        mbuf[(4 * Tr::NDT) * 64] = m_run;
+        mbuf[(4 * Tr::NDT + 1) * 64] = l_half;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+
+    const float m_o = mbuf[(4 * Tr::NDT) * 64];
+    const float l_o = mbuf[(4 * Tr::NDT + 1) * 64];
+    const float m_tot = fmaxf(m_run, m_o);
+    const float a_s = exp2_hw(m_run - m_tot);  // weight of this half
+    const float a_o = exp2_hw(m_o - m_tot);    // weight of the other half
+    const float l_tot = a_s * l_half + a_o * l_o;
     const float inv_own = 1.f / l_tot;
-    if (g == 0 && qrow < T) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_run + log2_hw(l_tot)) * kLn2;
+    if (g == 0 && qrow < T) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_tot + log2_hw(l_tot)) * kLn2;
+    const float f_s = a_s * inv_own, f_o = a_o * inv_own;
     float* Ob = O + ((size_t)b * Hq + h) * (size_t)T * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float inv = __shfl(inv_own, 4 * g + r);  // 1/l of query 16w + 4g + r
-        const int q = q0 + 16 * w + 4 * g + r;
+        const float fs = __shfl(f_s, 4 * g + r);  // factors of query 16rw + 4g + r
+        const float fo = __shfl(f_o, 4 * g + r);
+        const int q = q0 + 16 * rw + 4 * g + r;
+        float out[Tr::NDT];
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) out[dt] = acc[dt][r] * fs + mbuf[(4 * dt + r) * 64] * fo;
         if (q < T && (Tr::DP == D || li < D)) {
             float* dst = Ob + (size_t)q * D + Tr::NDT * li;
             if constexpr (Tr::NDT % 4 == 0) {
 #pragma unroll
                 for (int dt = 0; dt < Tr::NDT; dt += 4)
-                    *(f32x4*)(dst + dt) =
-                        f32x4{acc[dt][r] * inv, acc[dt + 1][r] * inv, acc[dt + 2][r] * inv, acc[dt + 3][r] * inv};
+                    *(f32x4*)(dst + dt) = f32x4{out[dt], out[dt + 1], out[dt + 2], out[dt + 3]};
             } else {
 #pragma unroll
-                for (int dt = 0; dt < Tr::NDT; ++dt) dst[dt] = acc[dt][r] * inv;
+                for (int dt = 0; dt < Tr::NDT; ++dt) dst[dt] = out[dt];
             }
         }
     }

@@ -43,6 +43,22 @@ __device__ __forceinline__ void pair_xor32(float x, float& a, float& b) {
     b = __uint_as_float(r[1]);
 }
 
+// Exchanges between two registers (gfx950 v_permlane16_swap / v_permlane32_swap):
+//   swap_rows16(a, b): the odd 16-lane rows of a trade places with the even rows of b,
+//     i.e. a = [a0, b0, a2, b2], b = [a1, b1, a3, b3] in 16-lane rows;
+//   swap_rows32(a, b): the upper half of a trades places with the lower half of b,
+//     i.e. a = [a0, a1, b0, b1], b = [a2, a3, b2, b3].
+__device__ __forceinline__ void swap_rows16(float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap_rows32(float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
 // Reductions over the four lanes l, l^16, l^32, l^48 (the four 16-lane rows),
 // i.e. over g for a fixed i.  Every lane of the group ends with the same bits.
 __device__ __forceinline__ float rows4_max(float x) {

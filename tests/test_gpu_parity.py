@@ -122,6 +122,36 @@ def test_gqa_backward_long_context(dev, orc):
         assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
 
 
+def _check_fwd_bwd(dev, orc, B, Hq, Hkv, T, D, seed):
+    host = si.causal_inputs(B, Hq, Hkv, T, D, seed=seed)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    ro, rlse = orc.causal_fwd(host["q"], host["k"], host["v"])
+    assert rel_err(o, ro) <= TOL_O and rel_err(lse, rlse) <= TOL_LSE, (rel_err(o, ro), rel_err(lse, rlse))
+    dq, dk, dv = _run_bwd(x, o, lse)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 32), (8, 4, 64)])
+def test_backward_whole_key_block_schedule(dev, orc, Hq, Hkv, D):
+    """More key blocks than two per CU: one work-group per whole key block."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    T = 600  # 10 key blocks, the last one ragged
+    B = (2 * cus + 10 * Hkv) // (10 * Hkv) + 1
+    assert B * Hkv * 10 > 2 * cus
+    announce(f"bwd whole-key-block schedule B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    _check_fwd_bwd(dev, orc, B, Hq, Hkv, T, D, seed=300 + D)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(1, 8, 2, 777, 32), (1, 1, 1, 1088, 64), (3, 6, 3, 960, 16)])
+def test_backward_half_pair_schedule(dev, orc, B, Hq, Hkv, T, D):
+    """Few key blocks: half pairs of key blocks per work-group, odd and even counts."""
+    announce(f"bwd half-pair schedule B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    _check_fwd_bwd(dev, orc, B, Hq, Hkv, T, D, seed=400 + T)
+
+
 # ---------------------------------------------------------------------------
 # invariants and closed forms on the GPU outputs
 # ---------------------------------------------------------------------------
