@@ -246,7 +246,7 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
         int cus = 0;
         ATTN_TRY(device_ready(&cus));
         attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, (float*)workspace,
-                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale};
+                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale, cus};
         return launched(attn::launch_paged_decode(a, (hipStream_t)stream), "attn_paged_decode launch");
     } catch (const std::exception& e) {
         return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_decode: ") + e.what());

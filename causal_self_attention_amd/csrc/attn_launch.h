@@ -32,6 +32,7 @@ struct DecodeArgs {
     float* partial;  // workspace (see decode_workspace_floats)
     int64_t S, Hq, Hkv, D, page_size, max_pages, num_pages;
     float scale;
+    int cu_count;  // compute units of the device (choice of the fused or the split path)
 };
 
 // Work ordering for triangular (causal) grids.  Work items are ranked heaviest

@@ -338,11 +338,20 @@ DECODE_CASES = [(D, G, ps) for D in (8, 16, 32, 64, 128) for G in (1, 4) for ps 
 DECODE_CASES += [(64, 8, 16), (32, 2, 32), (16, 8, 32)]
 
 
+def _decode_batch(dev, path, Hkv):
+    """Sequences per batch that select the split (few (sequence, KV head) pairs) or
+    the fused (at least half a CU count of pairs) decode path."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    return 5 if path == "split" else -(-cus // (2 * Hkv)) + 1
+
+
+@pytest.mark.parametrize("path", ["split", "fused"])
 @pytest.mark.parametrize("D,G,ps", DECODE_CASES)
-def test_decode_shapes(dev, orc, D, G, ps):
-    announce(f"decode D={D} G={G} page={ps}")
+def test_decode_shapes(dev, orc, D, G, ps, path):
     Hkv = 2
-    d = si.paged_decode_inputs(S=5, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=520,
+    S = _decode_batch(dev, path, Hkv)
+    announce(f"decode {path} S={S} D={D} G={G} page={ps}")
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=520,
                                max_pages=math.ceil(520 / ps) + 1, seed=100 + D + G + ps)
     d["context_lens"][0] = 1  # a single cached position
     o, lse = _decode(d, dev)
@@ -355,6 +364,22 @@ def test_decode_shapes(dev, orc, D, G, ps):
     # without lse
     o3, lse3 = _decode(d, dev, with_lse=False)
     assert lse3 is None and torch.equal(o3, o)
+
+
+@pytest.mark.parametrize("path", ["split", "fused"])
+def test_decode_long_context(dev, orc, path):
+    """A context longer than one pass of the fused waves (8 waves x 64 groups x 16)."""
+    Hkv, G, D, ps = 2, 4, 64, 64
+    S = _decode_batch(dev, path, Hkv)
+    announce(f"decode long context {path} S={S}")
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=9000,
+                               max_pages=math.ceil(9000 / ps), seed=77)
+    d["context_lens"][0] = 9000
+    d["context_lens"][1] = 8193
+    o, lse = _decode(d, dev)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE
 
 
 def test_decode_matches_causal_last_row(dev):
