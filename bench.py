@@ -214,6 +214,26 @@ def main():
     g_flops, _ = causal_flops(gcfg["B"], gcfg["Hq"], gcfg["T"], gcfg["D"])
     del gx, go, glse
 
+    # the step before decode: lease + append one token's K/V for every sequence of the
+    # decode workload's shape, into an empty cache (pages leased every 16th call)
+    S_, Hkv_, D_, ps_ = dcfg["S"], dcfg["Hkv"], dcfg["D"], dcfg["page_size"]
+    n_app = 64
+    cache = attn.PagedKvCache(S_, Hkv_, D_, ps_, n_app // ps_ + 1, S_ * (n_app // ps_ + 1), dev)
+    g_ = torch.Generator("cpu").manual_seed(6)
+    kn = torch.randn((S_, Hkv_, D_), generator=g_).to(dev)
+    vn = torch.randn((S_, Hkv_, D_), generator=g_).to(dev)
+    aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_app)]
+    torch.cuda.synchronize()
+    for a, b in aev:
+        a.record(stream)
+        attn.attn_kv_append(kn, vn, cache, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    if cache.status() != attn.ATTN_KV_OK:
+        raise RuntimeError("kv append refused during the bench")
+    app_us = statistics.median(a.elapsed_time(b) for a, b in aev) * 1e3
+    app_bytes = 2 * 2 * S_ * Hkv_ * D_ * 4  # new K and V rows read once and written once
+
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -259,6 +279,11 @@ def main():
         "gqa_t8192_fwd": {
             "ms_median": round(g_ms, 4), "tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 3),
             "frac_of_fp32_mfma_peak": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+        "kv_append": {
+            "us_median": round(app_us, 2), "bytes_per_call": app_bytes,
+            "gbps": round(app_bytes / (app_us * 1e-6) / 1e9, 2), "calls": n_app,
+            "note": "lease + append of one token for 32 sequences; two small launches, latency bound",
         },
         "wall_s_timed_region": round(wall, 4),
     }

@@ -24,7 +24,12 @@ ATTN_INVALID_ARGUMENT = 1
 ATTN_UNSUPPORTED = 2
 ATTN_WORKSPACE_TOO_SMALL = 3
 ATTN_DEVICE_ERROR = 4
-ATTN_ABI_VERSION = 0x00010000
+ATTN_ABI_VERSION = 0x00010001
+
+ATTN_KV_OK = 0
+ATTN_KV_POOL_EXHAUSTED = 1
+ATTN_KV_SEQUENCE_FULL = 2
+ATTN_KV_STACK_OVERFLOW = 3
 
 STATUS_NAMES = {
     ATTN_OK: "ATTN_OK",
@@ -50,6 +55,9 @@ SIGNATURES = {
     "attn_paged_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "attn_paged_decode": (_st, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _f, _vp, _vp, _vp, _sz, _vp]),
+    "attn_kv_append": (_st, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp]),
+    "attn_kv_release": (_st, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -205,3 +213,70 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
                                    workspace.numel() * workspace.element_size(),
                                    _stream_ptr(stream, dev)))
     return o, lse
+
+
+class PagedKvCache:
+    """Device state of one layer's paged K/V cache (tensors only; every update runs
+    in attn_kv_append / attn_kv_release).
+
+    k_pool, v_pool [num_pages, Hkv, page_size, D]; block_table [S, max_pages] and
+    context_lens [S] int32; free_pages [num_pages] int32 with free_count [1] (the
+    free-page stack, top at free_count - 1); kv_status [1] int32.  Starts empty:
+    every page free (the stack holds num_pages-1 .. 0, so page 0 is leased first),
+    every length 0.
+    """
+
+    def __init__(self, S, Hkv, D, page_size, max_pages, num_pages, device):
+        f32, i32 = torch.float32, torch.int32
+        self.S, self.Hkv, self.D = int(S), int(Hkv), int(D)
+        self.page_size, self.max_pages, self.num_pages = int(page_size), int(max_pages), int(num_pages)
+        self.k_pool = torch.zeros((num_pages, Hkv, page_size, D), device=device, dtype=f32)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.block_table = torch.zeros((S, max_pages), device=device, dtype=i32)
+        self.context_lens = torch.zeros((S,), device=device, dtype=i32)
+        self.free_pages = torch.arange(num_pages - 1, -1, -1, device=device, dtype=i32)
+        self.free_count = torch.full((1,), num_pages, device=device, dtype=i32)
+        self.kv_status = torch.zeros((1,), device=device, dtype=i32)
+
+    def append(self, k_new, v_new, stream=None):
+        attn_kv_append(k_new, v_new, self, stream=stream)
+
+    def release(self, seq_ids, stream=None):
+        attn_kv_release(seq_ids, self, stream=stream)
+
+    def status(self) -> int:
+        """Outcome of the last call (synchronizes with the device)."""
+        return int(self.kv_status.item())
+
+
+def attn_kv_append(k_new, v_new, cache, stream=None):
+    """Lease pages where needed and append k_new, v_new [S, Hkv, D] at each sequence's
+    current length (async; the outcome lands in cache.kv_status)."""
+    c = cache
+    dev = _same_device(k_new, v_new, c.k_pool)
+    if k_new.shape != (c.S, c.Hkv, c.D) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{c.S}, {c.Hkv}, {c.D}], got {tuple(k_new.shape)}")
+    _check(lib().attn_kv_append(_dev(k_new, "k_new"), _dev(v_new, "v_new"), c.S, c.Hkv, c.D, c.page_size,
+                                c.max_pages, c.num_pages, _dev(c.k_pool, "k_pool"), _dev(c.v_pool, "v_pool"),
+                                _dev(c.block_table, "block_table", torch.int32),
+                                _dev(c.context_lens, "context_lens", torch.int32),
+                                _dev(c.free_pages, "free_pages", torch.int32),
+                                _dev(c.free_count, "free_count", torch.int32),
+                                _dev(c.kv_status, "kv_status", torch.int32), _stream_ptr(stream, dev)))
+
+
+def attn_kv_release(seq_ids, cache, stream=None):
+    """Return the pages of sequences seq_ids (int32 device tensor of distinct indices)
+    to the free stack and zero their lengths (async)."""
+    c = cache
+    dev = _same_device(seq_ids, c.k_pool)
+    if seq_ids.dim() != 1:
+        raise ValueError("seq_ids must be 1-D")
+    n = seq_ids.numel()
+    ids_p = _dev(seq_ids, "seq_ids", torch.int32) if n > 0 else ctypes.c_void_p(0)
+    _check(lib().attn_kv_release(ids_p, n, c.S, c.page_size, c.max_pages, c.num_pages,
+                                 _dev(c.block_table, "block_table", torch.int32),
+                                 _dev(c.context_lens, "context_lens", torch.int32),
+                                 _dev(c.free_pages, "free_pages", torch.int32),
+                                 _dev(c.free_count, "free_count", torch.int32),
+                                 _dev(c.kv_status, "kv_status", torch.int32), _stream_ptr(stream, dev)))

@@ -255,4 +255,90 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
     }
 }
 
+// Sizes shared by the two K/V cache calls.
+static attn_status check_kv_shape(const char* fn, int64_t S, int64_t page_size, int64_t max_pages_per_seq,
+                                  int64_t num_pages) {
+    if (S <= 0 || page_size <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+        return fail(ATTN_INVALID_ARGUMENT,
+                    std::string(fn) + ": S, page_size, max_pages_per_seq and num_pages must all be positive");
+    if (page_size * max_pages_per_seq >= kMaxElems || S * max_pages_per_seq >= kMaxElems ||
+        num_pages >= kMaxElems)
+        return fail(ATTN_INVALID_ARGUMENT, std::string(fn) + ": sizes too large for int32 page ids and lengths");
+    if (page_size != 16 && page_size != 32 && page_size != 64)
+        return fail(ATTN_UNSUPPORTED, std::string(fn) + ": page_size " + std::to_string(page_size) +
+                                          " is not one of 16, 32, 64");
+    return ATTN_OK;
+}
+
+attn_status attn_kv_append(const float* k_new, const float* v_new, int64_t S, int64_t Hkv, int64_t D,
+                           int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages, float* k_pool,
+                           float* v_pool, int32_t* block_table, int32_t* context_lens, int32_t* free_pages,
+                           int32_t* free_count, int32_t* kv_status, void* stream) {
+    try {
+        ATTN_TRY(check_kv_shape("attn_kv_append", S, page_size, max_pages_per_seq, num_pages));
+        if (Hkv <= 0 || D <= 0) return fail(ATTN_INVALID_ARGUMENT, "attn_kv_append: Hkv and D must be positive");
+        if (num_pages * Hkv * page_size * D >= ((int64_t)1 << 40) || S * Hkv * D >= kMaxElems)
+            return fail(ATTN_INVALID_ARGUMENT, "attn_kv_append: pool or rows too large");
+        if (!attn::causal_head_dim_supported(D))
+            return fail(ATTN_UNSUPPORTED, "attn_kv_append: head width D=" + std::to_string(D) +
+                                              " is not one of 8, 16, 32, 64, 128");
+        ATTN_TRY(check_ptr(k_new, "k_new", 16));
+        ATTN_TRY(check_ptr(v_new, "v_new", 16));
+        ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
+        ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
+        ATTN_TRY(check_ptr(block_table, "block_table", 4));
+        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+        ATTN_TRY(check_ptr(free_pages, "free_pages", 4));
+        ATTN_TRY(check_ptr(free_count, "free_count", 4));
+        ATTN_TRY(check_ptr(kv_status, "kv_status", 4));
+        const size_t nb = (size_t)(S * Hkv * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
+        ATTN_TRY(check_disjoint({{k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
+                                 {block_table, (size_t)(S * max_pages_per_seq) * 4, "block_table"},
+                                 {context_lens, (size_t)S * 4, "context_lens"},
+                                 {free_pages, (size_t)num_pages * 4, "free_pages"}, {free_count, 4, "free_count"},
+                                 {kv_status, 4, "kv_status"}},
+                                {{k_new, nb, "k_new"}, {v_new, nb, "v_new"}}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::KvAppendArgs a{k_new, v_new, k_pool, v_pool, block_table, context_lens, free_pages, free_count,
+                             kv_status, S, Hkv, D, page_size, max_pages_per_seq, num_pages};
+        return launched(attn::launch_kv_append(a, (hipStream_t)stream), "attn_kv_append launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_kv_append: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_kv_append: unknown exception");
+    }
+}
+
+attn_status attn_kv_release(const int32_t* seq_ids, int64_t n, int64_t S, int64_t page_size,
+                            int64_t max_pages_per_seq, int64_t num_pages, int32_t* block_table,
+                            int32_t* context_lens, int32_t* free_pages, int32_t* free_count, int32_t* kv_status,
+                            void* stream) {
+    try {
+        ATTN_TRY(check_kv_shape("attn_kv_release", S, page_size, max_pages_per_seq, num_pages));
+        if (n < 0 || n > S)
+            return fail(ATTN_INVALID_ARGUMENT, "attn_kv_release: n must lie in [0, S] (ids are distinct)");
+        if (n > 0) ATTN_TRY(check_ptr(seq_ids, "seq_ids", 4));
+        ATTN_TRY(check_ptr(block_table, "block_table", 4));
+        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+        ATTN_TRY(check_ptr(free_pages, "free_pages", 4));
+        ATTN_TRY(check_ptr(free_count, "free_count", 4));
+        ATTN_TRY(check_ptr(kv_status, "kv_status", 4));
+        const Range ids{seq_ids, n > 0 ? (size_t)n * 4 : 0, "seq_ids"};
+        ATTN_TRY(check_disjoint({{context_lens, (size_t)S * 4, "context_lens"},
+                                 {free_pages, (size_t)num_pages * 4, "free_pages"}, {free_count, 4, "free_count"},
+                                 {kv_status, 4, "kv_status"}},
+                                {ids, {block_table, (size_t)(S * max_pages_per_seq) * 4, "block_table"}}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::KvReleaseArgs a{seq_ids, n, S, block_table, context_lens, free_pages, free_count, kv_status,
+                              page_size, max_pages_per_seq, num_pages};
+        return launched(attn::launch_kv_release(a, (hipStream_t)stream), "attn_kv_release launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_kv_release: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_kv_release: unknown exception");
+    }
+}
+
 }  // extern "C"

@@ -1,0 +1,175 @@
+// Paged K/V cache maintenance on gfx950: the step before single-token decode.
+//
+// What is computed: "Architecture", "Serving boundary" -- a request owns a
+// logical page table and the pool leases physical pages from shared per-layer
+// key/value pools; each new token's K/V is appended before attention reads it.
+// "Execution Backends and the Python ABI", "Incremental attention" -- pools are
+// [physical_page, H, page_offset, d_h] and the table maps logical to physical
+// page ids.
+//
+// The free pages form a stack in device memory (free_pages[0 .. free_count-1],
+// top at free_count-1), so leasing and releasing need no host round trip and the
+// whole serving step stays on the stream:
+//   1. attn_kv_lease (one work-group): finds the sequences whose next position
+//      starts a page, ranks them in index order with a block-wide scan and gives
+//      rank r the page free_pages[free_count - 1 - r].  If a sequence is full or
+//      the stack is short, it writes the status code and changes nothing.
+//   2. attn_kv_write (one work-group per sequence): if the status is OK, copies
+//      the token's Hkv x D key and value rows into their page slot (16-byte
+//      vectors) and advances the sequence's length.
+//   attn_kv_release (one work-group) pushes the pages of the given sequences
+//   back, in order, and zeroes their lengths.
+// The work is a few kilobytes per call; the kernels are latency bound by design
+// (one block-wide scan, one vector copy), not HBM bound.
+#include "attn_launch.h"
+#include "device_common.h"
+
+namespace attn {
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive prefix sum of x over the work-group (kScanThreads threads); the
+// group's total goes to *total.  Uses `buf` (kScanThreads ints of LDS).
+__device__ __forceinline__ int block_exclusive_scan(int x, int* buf, int* total) {
+    const int tid = threadIdx.x;
+    buf[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {  // Hillis-Steele inclusive scan
+        const int y = tid >= off ? buf[tid - off] : 0;
+        __syncthreads();
+        buf[tid] += y;
+        __syncthreads();
+    }
+    const int incl = buf[tid];
+    *total = buf[kScanThreads - 1];
+    __syncthreads();  // buf is reused by the next call
+    return incl - x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void attn_kv_lease_kernel(
+    int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, const int32_t* __restrict__ FREE,
+    int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int PS, int max_pages) {
+    __shared__ int buf[kScanThreads];
+    const int tid = threadIdx.x;
+    const int cap = PS * max_pages;
+    // pass 1: how many sequences start a page, and is any sequence full
+    int needed = 0, full = 0;
+    for (int base = 0; base < S; base += kScanThreads) {
+        const int s = base + tid;
+        const int t = s < S ? CTX[s] : 1;
+        int tot;
+        block_exclusive_scan(s < S && t >= cap ? 1 : 0, buf, &tot);
+        full += tot;
+        block_exclusive_scan(s < S && t >= 0 && t < cap && t % PS == 0 ? 1 : 0, buf, &tot);
+        needed += tot;
+    }
+    const int top = *FCOUNT;
+    if (full > 0 || needed > top) {
+        if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
+        return;  // uniform
+    }
+    // pass 2: rank r (index order) takes free_pages[top - 1 - r]
+    int offset = 0;
+    for (int base = 0; base < S; base += kScanThreads) {
+        const int s = base + tid;
+        const int t = s < S ? CTX[s] : 1;
+        const bool need = s < S && t >= 0 && t % PS == 0;  // t < cap: no sequence is full here
+        int tot;
+        const int rank = offset + block_exclusive_scan(need ? 1 : 0, buf, &tot);
+        if (need) BT[(size_t)s * max_pages + t / PS] = FREE[top - 1 - rank];
+        offset += tot;
+    }
+    if (tid == 0) {
+        *FCOUNT = top - needed;
+        *STATUS = ATTN_KV_OK;
+    }
+}
+
+__global__ __launch_bounds__(256) void attn_kv_write_kernel(
+    const float* __restrict__ Kn, const float* __restrict__ Vn, float* __restrict__ Kp, float* __restrict__ Vp,
+    const int32_t* __restrict__ BT, int32_t* __restrict__ CTX, const int32_t* __restrict__ STATUS, int Hkv,
+    int D, int PS, int max_pages, int num_pages) {
+    if (*STATUS != ATTN_KV_OK) return;  // uniform: the lease failed, change nothing
+    const int s = blockIdx.x;
+    const int t = CTX[s];
+    if (t < 0) return;  // uniform; a broken length (the lease found no sequence full, so t < cap)
+    // a table entry outside the pool (a broken state) is clamped: wrong data, never an
+    // out-of-bounds write
+    const int page = min(max(BT[(size_t)s * max_pages + t / PS], 0), num_pages - 1);
+    const int d4 = D / 4;
+    for (int idx = threadIdx.x; idx < Hkv * d4; idx += blockDim.x) {
+        const int h = idx / d4, c = idx % d4;
+        const size_t src = ((size_t)s * Hkv + h) * D + 4 * c;
+        const size_t dst = (((size_t)page * Hkv + h) * PS + t % PS) * D + 4 * c;
+        *(f32x4*)(Kp + dst) = *(const f32x4*)(Kn + src);
+        *(f32x4*)(Vp + dst) = *(const f32x4*)(Vn + src);
+    }
+    __syncthreads();  // every thread has used t
+    if (threadIdx.x == 0) CTX[s] = t + 1;
+}
+
+__global__ __launch_bounds__(kScanThreads) void attn_kv_release_kernel(
+    const int32_t* __restrict__ IDS, int n, int32_t* __restrict__ BT, int32_t* __restrict__ CTX,
+    int32_t* __restrict__ FREE, int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int PS,
+    int max_pages, int num_pages) {
+    __shared__ int buf[kScanThreads];
+    const int tid = threadIdx.x;
+    const int cap = PS * max_pages;
+    auto pages_of = [&](int i) -> int {  // pages held by sequence IDS[i] (0 for an index out of range)
+        if (i >= n) return 0;
+        const int s = IDS[i];
+        if (s < 0 || s >= S) return 0;
+        const int t = min(max(CTX[s], 0), cap);
+        return (t + PS - 1) / PS;
+    };
+    int total = 0;
+    for (int base = 0; base < n; base += kScanThreads) {
+        int tot;
+        block_exclusive_scan(pages_of(base + tid), buf, &tot);
+        total += tot;
+    }
+    const int top = *FCOUNT;
+    if (top + total > num_pages) {
+        if (tid == 0) *STATUS = ATTN_KV_STACK_OVERFLOW;
+        return;  // uniform
+    }
+    int offset = 0;
+    for (int base = 0; base < n; base += kScanThreads) {
+        const int i = base + tid;
+        const int np = pages_of(i);
+        int tot;
+        const int at = top + offset + block_exclusive_scan(np, buf, &tot);
+        for (int p = 0; p < np; ++p) FREE[at + p] = BT[(size_t)IDS[i] * max_pages + p];
+        offset += tot;
+    }
+    __syncthreads();  // every length has been read
+    for (int base = 0; base < n; base += kScanThreads) {
+        const int i = base + tid;
+        if (i < n && IDS[i] >= 0 && IDS[i] < S) CTX[IDS[i]] = 0;
+    }
+    if (tid == 0) {
+        *FCOUNT = top + total;
+        *STATUS = ATTN_KV_OK;
+    }
+}
+
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_kv_lease_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.block_table,
+                       a.context_lens, a.free_pages, a.free_count, a.status, (int)a.S, (int)a.page_size,
+                       (int)a.max_pages);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_kv_write_kernel, dim3((unsigned)a.S), dim3(256), 0, stream, a.k_new, a.v_new,
+                       a.k_pool, a.v_pool, a.block_table, a.context_lens, a.status, (int)a.Hkv, (int)a.D,
+                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages);
+    return hipGetLastError();
+}
+
+hipError_t launch_kv_release(const KvReleaseArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_kv_release_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.seq_ids, (int)a.n,
+                       a.block_table, a.context_lens, a.free_pages, a.free_count, a.status, (int)a.S,
+                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/attn.h"
+
 namespace attn {
 
 struct FwdArgs {
@@ -35,6 +37,20 @@ struct DecodeArgs {
     int cu_count;  // compute units of the device (choice of the fused or the split path)
 };
 
+struct KvAppendArgs {
+    const float *k_new, *v_new;
+    float *k_pool, *v_pool;
+    int32_t *block_table, *context_lens, *free_pages, *free_count, *status;
+    int64_t S, Hkv, D, page_size, max_pages, num_pages;
+};
+
+struct KvReleaseArgs {
+    const int32_t* seq_ids;
+    int64_t n, S;
+    int32_t *block_table, *context_lens, *free_pages, *free_count, *status;
+    int64_t page_size, max_pages, num_pages;
+};
+
 // Work ordering for triangular (causal) grids.  Work items are ranked heaviest
 // first; work-group ids are dealt to the compute units in rounds of `ncu`, and
 // every second round is reversed, so the work-groups that end up sharing a
@@ -58,5 +74,7 @@ size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, in
 hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_release(const KvReleaseArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -15,6 +15,12 @@
  *   attn_paged_decode  single-token decode over a paged K/V cache addressed
  *                      through per-sequence block tables ("Execution Backends
  *                      and the Python ABI", "Incremental attention").
+ *   attn_kv_append     the step before decode: lease pages from a device-resident
+ *   attn_kv_release    free list and append each sequence's newest K/V rows, or
+ *                      return a finished sequence's pages ("Architecture",
+ *                      "Serving boundary": a request's logical page table, pages
+ *                      leased from shared per-layer pools; "Incremental
+ *                      attention": [physical_page, H, page_offset, d_h] pools).
  *
  * Conventions ("Architecture", "Tensor conventions"): contiguous row-major
  * float32; scores are [B,H,Tq,Tk] with Tq = Tk = T; the key at position t_k is
@@ -47,7 +53,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 0x00010000u /* 1.0: major << 16 | minor */
+#define ATTN_ABI_VERSION 0x00010001u /* 1.1: major << 16 | minor */
 
 typedef int32_t attn_status;
 enum {
@@ -144,6 +150,65 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
                               int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
                               float scale, float* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Paged K/V cache maintenance: the step before attn_paged_decode.
+ *
+ * State, all in device memory and owned by the caller (one set per layer):
+ *   k_pool, v_pool  [num_pages, Hkv, page_size, D] float32
+ *   block_table     [S, max_pages_per_seq] int32   logical page -> physical page
+ *   context_lens    [S] int32                      cached positions per sequence
+ *   free_pages      [num_pages] int32              stack of free physical pages;
+ *   free_count      [1] int32                      entries 0 .. free_count-1 are free,
+ *                                                  free_pages[free_count-1] is the top
+ *   kv_status       [1] int32                      outcome of the last call (below)
+ * Initial state: every page free (free_pages a permutation of 0 .. num_pages-1,
+ * free_count = num_pages), every context length 0.
+ *
+ * The outcome is written to kv_status on the device, because the calls do not
+ * wait for the stream: ATTN_KV_OK, or one of the codes below, in which case the
+ * call changed nothing else.
+ */
+enum {
+    ATTN_KV_OK = 0,
+    ATTN_KV_POOL_EXHAUSTED = 1, /* append: fewer free pages than sequences starting a page */
+    ATTN_KV_SEQUENCE_FULL = 2,  /* append: a sequence already holds max_pages_per_seq * page_size */
+    ATTN_KV_STACK_OVERFLOW = 3  /* release: the free stack would exceed num_pages (a page
+                                   released twice) */
+};
+
+/*
+ * Appends one position to each of the S sequences:
+ *   k_new, v_new  [S, Hkv, D] float32   the newest token's key and value rows
+ * For sequence s with t = context_lens[s]: when t % page_size == 0 a page is
+ * leased first -- sequences needing one are ranked in index order and rank r
+ * takes free_pages[free_count - 1 - r]; free_count drops by their number -- and
+ * recorded as block_table[s, t / page_size].  Then
+ *   k_pool[block_table[s, t / page_size], h, t % page_size, :] = k_new[s, h, :]
+ * (same for v) for every KV head h, and context_lens[s] = t + 1.
+ * k_new, v_new, pools 16-byte aligned; the int32 arrays 4-byte aligned; no
+ * output overlaps an input or another output.  D and page_size as for
+ * attn_paged_decode.  Device-side precondition: the state is consistent (every
+ * page of a live sequence is outside the free stack, and the table entries below
+ * ceil(context_lens[s] / page_size) are its pages).
+ */
+attn_status attn_kv_append(const float* k_new, const float* v_new,
+                           int64_t S, int64_t Hkv, int64_t D,
+                           int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
+                           float* k_pool, float* v_pool, int32_t* block_table, int32_t* context_lens,
+                           int32_t* free_pages, int32_t* free_count, int32_t* kv_status, void* stream);
+
+/*
+ * Returns the pages of sequences seq_ids[0 .. n-1] (distinct indices in [0, S))
+ * to the free stack and sets their context lengths to 0.  The pages are pushed
+ * in order: sequence seq_ids[0]'s logical pages 0, 1, ..., then seq_ids[1]'s, ...
+ * (the last one pushed is the next one leased).  seq_ids 4-byte aligned device
+ * memory; n >= 0 (n == 0 does nothing but write ATTN_KV_OK).
+ */
+attn_status attn_kv_release(const int32_t* seq_ids, int64_t n, int64_t S,
+                            int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
+                            int32_t* block_table, int32_t* context_lens,
+                            int32_t* free_pages, int32_t* free_count, int32_t* kv_status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -54,7 +54,7 @@ def test_header_is_c11_clean(tmp_path):
 
 
 def test_version_and_status_values(L):
-    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010000
+    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010001
     header = open(HEADER).read()
     for name in ("ATTN_OK", "ATTN_INVALID_ARGUMENT", "ATTN_UNSUPPORTED", "ATTN_WORKSPACE_TOO_SMALL",
                  "ATTN_DEVICE_ERROR"):
@@ -102,6 +102,22 @@ def _dec(L, S=2, Hq=4, Hkv=2, D=64, page=16, maxp=8, npages=16, scale=0.125, ws_
         ws_bytes = attn.attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page, maxp)
     return L.attn_paged_decode(p["q"], p["kp"], p["vp"], p["bt"], p["ctx"], S, Hq, Hkv, D, page, maxp, npages,
                                scale, p["o"], p["lse"], p["ws"], ws_bytes, None)
+
+
+def _app(L, S=3, Hkv=2, D=64, page=16, maxp=4, npages=8, **ptrs):
+    names = ["kn", "vn", "kp", "vp", "bt", "ctx", "free", "fc", "st"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_kv_append(p["kn"], p["vn"], S, Hkv, D, page, maxp, npages, p["kp"], p["vp"], p["bt"], p["ctx"],
+                            p["free"], p["fc"], p["st"], None)
+
+
+def _rel(L, n=2, S=3, page=16, maxp=4, npages=8, **ptrs):
+    names = ["ids", "bt", "ctx", "free", "fc", "st"]
+    p = {n_: _p(i) for i, n_ in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_kv_release(p["ids"], n, S, page, maxp, npages, p["bt"], p["ctx"], p["free"], p["fc"], p["st"],
+                             None)
 
 
 def _expect(status, want, fragment):
@@ -153,6 +169,23 @@ def test_decode_invalid_arguments(L):
     _expect(_dec(L, bt=ctypes.c_void_p(0x400000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
 
 
+def test_kv_invalid_arguments(L):
+    _expect(_app(L, kn=None), attn.ATTN_INVALID_ARGUMENT, "'k_new' is NULL")
+    _expect(_app(L, st=None), attn.ATTN_INVALID_ARGUMENT, "'kv_status' is NULL")
+    _expect(_app(L, S=0), attn.ATTN_INVALID_ARGUMENT, "positive")
+    _expect(_app(L, Hkv=0), attn.ATTN_INVALID_ARGUMENT, "positive")
+    _expect(_app(L, page=24), attn.ATTN_UNSUPPORTED, "page_size 24")
+    _expect(_app(L, D=40), attn.ATTN_UNSUPPORTED, "D=40")
+    _expect(_app(L, kp=ctypes.c_void_p(0x300000004)), attn.ATTN_INVALID_ARGUMENT, "aligned")
+    _expect(_app(L, kp=_p(0)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'k_new'")
+    _expect(_app(L, fc=_p(6)), attn.ATTN_INVALID_ARGUMENT, "overlap")  # free_count inside free_pages
+    _expect(_rel(L, ids=None), attn.ATTN_INVALID_ARGUMENT, "'seq_ids' is NULL")
+    _expect(_rel(L, n=4), attn.ATTN_INVALID_ARGUMENT, "[0, S]")
+    _expect(_rel(L, n=-1), attn.ATTN_INVALID_ARGUMENT, "[0, S]")
+    _expect(_rel(L, page=128), attn.ATTN_UNSUPPORTED, "page_size 128")
+    _expect(_rel(L, ctx=_p(0)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'seq_ids'")
+
+
 def _gpu_present():
     try:
         import torch
@@ -176,6 +209,8 @@ def test_valid_call_without_device_reports_device_error(L):
     _expect(_fwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_bwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_dec(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_app(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_rel(L), attn.ATTN_DEVICE_ERROR, "device")
 
 
 def test_success_clears_nothing_spurious(L):
