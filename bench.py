@@ -10,8 +10,9 @@ All inputs are generated once and already resident in HBM when timing starts.
 Printed: one JSON line.  `value` is the causal forward+backward rate in
 algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
 QK^T recompute, dV, dP, dK, dQ backward) over the summed event times of the two
-calls; the decode rate (algorithmic HBM bytes per call / call time) and the
-8192-token grouped-query forward are reported beside it.  Each decode call
+calls; the decode rate (algorithmic HBM bytes per call / call time), the
+8192-token grouped-query forward and backward and the latency of a K/V append
+(the step before decode) are reported beside it.  Each decode call
 reads a different one of several pool replicas so the 256 MB last-level cache
 cannot serve a repeated pool.
 
@@ -195,9 +196,10 @@ def main():
     dec_avg_s = sum(t_dec) / K * 1e-3
     dec_gbps = dbytes / dec_avg_s / 1e9
 
-    # the 8192-token grouped-query forward (O + LSE), timed separately
+    # the 8192-token grouped-query forward (O + LSE), timed separately, then its
+    # backward (dO drawn after Q, K, V with the same generator)
     gcfg = si.CAUSAL_WORKLOADS[GQA]
-    gh = si.causal_workload(GQA)
+    gh = si.causal_inputs(gcfg["B"], gcfg["Hq"], gcfg["Hkv"], gcfg["T"], gcfg["D"], gcfg["seed"], with_do=True)
     gx = {k: v.to(dev) for k, v in gh.items()}
     go = torch.empty_like(gx["q"])
     glse = torch.empty((gcfg["B"], gcfg["Hq"], gcfg["T"]), device=dev)
@@ -211,8 +213,21 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     g_ms = statistics.median(a.elapsed_time(b) for a, b in gev)
-    g_flops, _ = causal_flops(gcfg["B"], gcfg["Hq"], gcfg["T"], gcfg["D"])
-    del gx, go, glse
+    g_flops, g_bflops = causal_flops(gcfg["B"], gcfg["Hq"], gcfg["T"], gcfg["D"])
+    gdq, gdk, gdv = torch.empty_like(gx["q"]), torch.empty_like(gx["k"]), torch.empty_like(gx["v"])
+    gws = torch.empty((attn.attn_causal_bwd_workspace_bytes(gcfg["B"], gcfg["Hq"], gcfg["Hkv"], gcfg["T"],
+                                                            gcfg["D"]) // 4,), device=dev)
+    attn.attn_causal_bwd(gx["q"], gx["k"], gx["v"], go, glse, gx["dout"], dq=gdq, dk=gdk, dv=gdv, workspace=gws,
+                         stream=stream)
+    torch.cuda.synchronize()
+    for a, b in gev:
+        a.record(stream)
+        attn.attn_causal_bwd(gx["q"], gx["k"], gx["v"], go, glse, gx["dout"], dq=gdq, dk=gdk, dv=gdv,
+                             workspace=gws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    gb_ms = statistics.median(a.elapsed_time(b) for a, b in gev)
+    del gx, go, glse, gdq, gdk, gdv, gws
 
     # the step before decode: lease + append one token's K/V for every sequence of the
     # decode workload's shape, into an empty cache (pages leased every 16th call)
@@ -279,6 +294,13 @@ def main():
         "gqa_t8192_fwd": {
             "ms_median": round(g_ms, 4), "tflops": round(g_flops / (g_ms * 1e-3) / 1e12, 3),
             "frac_of_fp32_mfma_peak": round(g_flops / (g_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+        "gqa_t8192_fwd_bwd": {
+            "fwd_ms_median": round(g_ms, 4), "bwd_ms_median": round(gb_ms, 4),
+            "bwd_tflops": round(g_bflops / (gb_ms * 1e-3) / 1e12, 3),
+            "tflops": round((g_flops + g_bflops) / ((g_ms + gb_ms) * 1e-3) / 1e12, 3),
+            "frac_of_fp32_mfma_peak": round((g_flops + g_bflops) / ((g_ms + gb_ms) * 1e-3) / 1e12
+                                            / PEAK_FP32_MFMA_TFLOPS, 4),
         },
         "kv_append": {
             "us_median": round(app_us, 2), "bytes_per_call": app_bytes,

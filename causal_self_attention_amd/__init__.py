@@ -30,3 +30,4 @@ from ._binding import (  # noqa: F401
     lib,
     library_path,
 )
+from .autograd import CausalAttentionFunction, causal_attention  # noqa: F401
