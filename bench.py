@@ -229,6 +229,28 @@ def main():
     gb_ms = statistics.median(a.elapsed_time(b) for a, b in gev)
     del gx, go, glse, gdq, gdk, gdv, gws
 
+    # the materialized path on the 1024-token workload: O, LSE and P [B,H,T,T] forward,
+    # the VJP from the stored P
+    mp = torch.empty((B, Hq, T, T), device=dev)
+    mdq, mdk, mdv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    mev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
+    for it in range(12):
+        ev = mev[it - 2] if it >= 2 else None
+        if ev:
+            ev[0].record(stream)
+        attn.attn_materialized_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, p=mp, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        attn.attn_materialized_bwd(x["q"], x["k"], x["v"], o, mp, x["dout"], dq=mdq, dk=mdk, dv=mdv, workspace=ws,
+                                   stream=stream)
+        if ev:
+            ev[2].record(stream)
+    torch.cuda.synchronize()
+    m_fwd_us = statistics.median(e[0].elapsed_time(e[1]) for e in mev) * 1e3
+    m_bwd_us = statistics.median(e[1].elapsed_time(e[2]) for e in mev) * 1e3
+    p_bytes = B * Hq * T * T * 4
+    del mp, mdq, mdk, mdv
+
     # the step before decode: lease + append one token's K/V for every sequence of the
     # decode workload's shape, into an empty cache (pages leased every 16th call)
     S_, Hkv_, D_, ps_ = dcfg["S"], dcfg["Hkv"], dcfg["D"], dcfg["page_size"]
@@ -301,6 +323,11 @@ def main():
             "tflops": round((g_flops + g_bflops) / ((g_ms + gb_ms) * 1e-3) / 1e12, 3),
             "frac_of_fp32_mfma_peak": round((g_flops + g_bflops) / ((g_ms + gb_ms) * 1e-3) / 1e12
                                             / PEAK_FP32_MFMA_TFLOPS, 4),
+        },
+        "materialized": {
+            "workload": CAUSAL, "fwd_us_median": round(m_fwd_us, 2), "bwd_us_median": round(m_bwd_us, 2),
+            "p_bytes": p_bytes, "fwd_p_store_gbps": round(p_bytes / (m_fwd_us * 1e-6) / 1e9, 1),
+            "bwd_tflops": round(bwd_flops / (m_bwd_us * 1e-6) / 1e12, 3),
         },
         "kv_append": {
             "us_median": round(app_us, 2), "bytes_per_call": app_bytes,

@@ -1,5 +1,6 @@
-"""MI355X (gfx950) causal attention: flash-style forward, its VJP, paged decode
-and the paged K/V cache it reads (page leasing and appends).
+"""MI355X (gfx950) causal attention: flash-style forward, its VJP, the
+materialized path (probabilities as an output), paged decode and the paged K/V
+cache it reads (page leasing and appends).
 
 The computation runs in the HIP kernels of ``libattn.so`` behind a C ABI
 (``include/attn.h``); this package is a thin ctypes binding with the same
@@ -25,6 +26,9 @@ from ._binding import (  # noqa: F401
     attn_kv_append,
     attn_kv_release,
     attn_last_error,
+    attn_materialized_bwd,
+    attn_materialized_bwd_workspace_bytes,
+    attn_materialized_fwd,
     attn_paged_decode,
     attn_paged_decode_workspace_bytes,
     lib,

@@ -24,7 +24,7 @@ ATTN_INVALID_ARGUMENT = 1
 ATTN_UNSUPPORTED = 2
 ATTN_WORKSPACE_TOO_SMALL = 3
 ATTN_DEVICE_ERROR = 4
-ATTN_ABI_VERSION = 0x00010001
+ATTN_ABI_VERSION = 0x00010002
 
 ATTN_KV_OK = 0
 ATTN_KV_POOL_EXHAUSTED = 1
@@ -55,6 +55,10 @@ SIGNATURES = {
     "attn_paged_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "attn_paged_decode": (_st, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _f, _vp, _vp, _vp, _sz, _vp]),
+    "attn_materialized_fwd": (_st, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f, _vp, _vp, _vp, _vp]),
+    "attn_materialized_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "attn_materialized_bwd": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f,
+                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     "attn_kv_append": (_st, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp]),
     "attn_kv_release": (_st, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -213,6 +217,52 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
                                    workspace.numel() * workspace.element_size(),
                                    _stream_ptr(stream, dev)))
     return o, lse
+
+
+def attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D) -> int:
+    return int(lib().attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D))
+
+
+def attn_materialized_fwd(q, k, v, scale=None, o=None, lse=None, p=None, stream=None):
+    """O [B,Hq,T,D], LSE [B,Hq,T] and the probabilities P [B,Hq,T,T] (async)."""
+    dev = _same_device(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"expected q [B,Hq,T,D], k/v [B,Hkv,T,D]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, T), device=dev, dtype=torch.float32)
+    if p is None:
+        p = torch.empty((B, Hq, T, T), device=dev, dtype=torch.float32)
+    _check(lib().attn_materialized_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, T, D, scale,
+                                       _dev(o, "o"), _dev(lse, "lse"), _dev(p, "p"), _stream_ptr(stream, dev)))
+    return o, lse, p
+
+
+def attn_materialized_bwd(q, k, v, o, p, dout, dp=None, scale=None, dq=None, dk=None, dv=None, workspace=None,
+                          stream=None):
+    """(dQ, dK, dV) of sum(dout * O) + sum(dp * P) using the stored probabilities p (async)."""
+    dev = _same_device(q, k, v, o, p, dout)
+    B, Hq, T, D = q.shape
+    Hkv = k.shape[1]
+    if p.shape != (B, Hq, T, T) or (dp is not None and dp.shape != p.shape):
+        raise ValueError("p (and dp) must be [B, Hq, T, T]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
+    dp_p = _dev(dp, "dp") if dp is not None else ctypes.c_void_p(0)
+    _check(lib().attn_materialized_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(p, "p"),
+                                       _dev(dout, "dout"), dp_p, B, Hq, Hkv, T, D, scale, _dev(dq, "dq"),
+                                       _dev(dk, "dk"), _dev(dv, "dv"), _dev(workspace, "workspace"),
+                                       workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev)))
+    return dq, dk, dv
 
 
 class PagedKvCache:

@@ -255,6 +255,78 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
     }
 }
 
+attn_status attn_materialized_fwd(const float* q, const float* k, const float* v, int64_t B, int64_t Hq,
+                                  int64_t Hkv, int64_t T, int64_t D, float scale, float* o, float* lse, float* p,
+                                  void* stream) {
+    try {
+        ATTN_TRY(check_causal_shape(B, Hq, Hkv, T, D, scale));
+        if (B * Hq * T * T >= ((int64_t)1 << 40))
+            return fail(ATTN_INVALID_ARGUMENT, "attn_materialized_fwd: B*Hq*T*T must stay below 2^40");
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k, "k", 16));
+        ATTN_TRY(check_ptr(v, "v", 16));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        ATTN_TRY(check_ptr(lse, "lse", 4));
+        ATTN_TRY(check_ptr(p, "p", 16));
+        const size_t qb = (size_t)(B * Hq * T * D) * 4, kb = (size_t)(B * Hkv * T * D) * 4;
+        const size_t lb = (size_t)(B * Hq * T) * 4, pb = (size_t)(B * Hq * T * T) * 4;
+        ATTN_TRY(check_disjoint({{o, qb, "o"}, {lse, lb, "lse"}, {p, pb, "p"}},
+                                {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::MatFwdArgs a{q, k, v, o, lse, p, B, Hq, Hkv, T, D, scale, cus};
+        return launched(attn::launch_materialized_fwd(a, (hipStream_t)stream), "attn_materialized_fwd launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_materialized_fwd: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_materialized_fwd: unknown exception");
+    }
+}
+
+size_t attn_materialized_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D) {
+    return attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D);
+}
+
+attn_status attn_materialized_bwd(const float* q, const float* k, const float* v, const float* o, const float* p,
+                                  const float* dout, const float* dp, int64_t B, int64_t Hq, int64_t Hkv, int64_t T,
+                                  int64_t D, float scale, float* dq, float* dk, float* dv, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    try {
+        ATTN_TRY(check_causal_shape(B, Hq, Hkv, T, D, scale));
+        if (B * Hq * T * T >= ((int64_t)1 << 40))
+            return fail(ATTN_INVALID_ARGUMENT, "attn_materialized_bwd: B*Hq*T*T must stay below 2^40");
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k, "k", 16));
+        ATTN_TRY(check_ptr(v, "v", 16));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        ATTN_TRY(check_ptr(p, "p", 4));
+        ATTN_TRY(check_ptr(dout, "dout", 16));
+        if (dp) ATTN_TRY(check_ptr(dp, "dp", 4));
+        ATTN_TRY(check_ptr(dq, "dq", 16));
+        ATTN_TRY(check_ptr(dk, "dk", 16));
+        ATTN_TRY(check_ptr(dv, "dv", 16));
+        ATTN_TRY(check_ptr(workspace, "workspace", 16));
+        const size_t need = attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D);
+        if (workspace_bytes < need)
+            return fail(ATTN_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) +
+                                                      " bytes, attn_materialized_bwd needs " + std::to_string(need));
+        const size_t qb = (size_t)(B * Hq * T * D) * 4, kb = (size_t)(B * Hkv * T * D) * 4;
+        const size_t pb = (size_t)(B * Hq * T * T) * 4;
+        const Range dpr{dp, dp ? pb : 0, "dp"};
+        ATTN_TRY(check_disjoint({{dq, qb, "dq"}, {dk, kb, "dk"}, {dv, kb, "dv"}, {workspace, need, "workspace"}},
+                                {{q, qb, "q"}, {k, kb, "k"}, {v, kb, "v"}, {o, qb, "o"}, {p, pb, "p"},
+                                 {dout, qb, "dout"}, dpr}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::BwdArgs a{q, k, v, o, nullptr, dout, dq, dk, dv, (float*)workspace, B, Hq, Hkv, T, D, scale, cus, p, dp};
+        return launched(attn::launch_materialized_bwd(a, (hipStream_t)stream), "attn_materialized_bwd launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_materialized_bwd: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_materialized_bwd: unknown exception");
+    }
+}
+
 // Sizes shared by the two K/V cache calls.
 static attn_status check_kv_shape(const char* fn, int64_t S, int64_t page_size, int64_t max_pages_per_seq,
                                   int64_t num_pages) {

@@ -117,10 +117,14 @@ __device__ __forceinline__ void lds_row(const float* p, float (&x)[N]) {
     }
 }
 
-template <int D>
+// MAT (the materialized variant): the probabilities come from a stored P
+// [B,Hq,T,T] instead of exp(s - LSE), so S = Q K^T is not formed; dPx (may be
+// NULL) is a cotangent of P itself, added to dP.
+template <int D, bool MAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 1 : 2, D >= 128 ? 1 : 2))) void attn_bwd_main_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
+    const float* __restrict__ P, const float* __restrict__ dPx,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
     int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
             const int d0 = 4 * Tr::W * u + Tr::W * g;
             if constexpr (Tr::W == 4) {
-                f32x4 x = keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 x = !MAT && keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
                 f32x4 y = keyw < T ? *(const f32x4*)(Vh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                     vf[4 * u + j] = y[j];
                 }
             } else {
-                f32x2 x = keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+                f32x2 x = !MAT && keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
                 f32x2 y = keyw < T ? *(const f32x2*)(Vh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
                 kf[2 * u] = x[0];
                 kf[2 * u + 1] = x[1];
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
             if (tid < Tr::BM) {
                 const int q = q0 + tid;
                 // a padding row gets LSE = +inf, so its probabilities are exactly 0
-                xl = q < T ? LSE[hoff + q] * kLog2e : INFINITY;
+                xl = !MAT && q < T ? LSE[hoff + q] * kLog2e : INFINITY;
                 xd = q < T ? Delta[hoff + q] : 0.f;
             }
         };
@@ -300,12 +304,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 // then copies the accumulators at every join, which costs more than it saves.
                 const bool diag = (qb == kb);
 
-                // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li]
+                // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li].  MAT: S is not
+                // formed; sa takes the stored P of this lane's (query, key) entries and dP
+                // starts from the cotangent of P.
                 f32x4 sa[4], pa[4];
 #pragma unroll
                 for (int qs = 0; qs < 4; ++qs) {
                     sa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
                     pa[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (MAT) {
+                        const size_t prow = ((size_t)b * Hq + h) * (size_t)T;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int q = q0 + 16 * qs + 4 * g + r;
+                            const bool in = q < T && keyw < T;
+                            const size_t at = (prow + (in ? q : 0)) * (size_t)T + (in ? keyw : 0);
+                            sa[qs][r] = in ? P[at] : 0.f;
+                            if (dPx) pa[qs][r] = in ? dPx[at] : 0.f;
+                        }
+                    }
                     {
 #pragma unroll
                         for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
@@ -315,7 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                                 const f32x4 c = *(const f32x4*)&dOs[off];
 #pragma unroll
                                 for (int j = 0; j < 4; ++j) {
-                                    sa[qs] = mfma16x16x4(a[j], kf[4 * u + j], sa[qs]);
+                                    if constexpr (!MAT) sa[qs] = mfma16x16x4(a[j], kf[4 * u + j], sa[qs]);
                                     pa[qs] = mfma16x16x4(c[j], vf[4 * u + j], pa[qs]);
                                 }
                             } else {
@@ -323,7 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                                 const f32x2 c = *(const f32x2*)&dOs[off];
 #pragma unroll
                                 for (int j = 0; j < 2; ++j) {
-                                    sa[qs] = mfma16x16x4(a[j], kf[2 * u + j], sa[qs]);
+                                    if constexpr (!MAT) sa[qs] = mfma16x16x4(a[j], kf[2 * u + j], sa[qs]);
                                     pa[qs] = mfma16x16x4(c[j], vf[2 * u + j], pa[qs]);
                                 }
                             }
@@ -340,7 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int qr = 16 * qs + 4 * g + r;  // row within the tile
-                        float p = exp2_hw(sa[qs][r] * c2 - l4[r]);
+                        float p = MAT ? sa[qs][r] : exp2_hw(sa[qs][r] * c2 - l4[r]);
                         p = (diag && 16 * w + li > qr) ? 0.f : p;
                         const float ds = scale * p * (pa[qs][r] - d4[r]);
                         sa[qs][r] = p;
@@ -481,7 +498,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     }
 }
 
-template <int D>
+template <int D, bool MAT>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     using Tr = BwdTraits<D>;
     const int nkb = (int)((a.T + Tr::BN - 1) / Tr::BN);
@@ -501,10 +518,14 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
                        a.delta, a.dq, rows, a.dk, a.dv, a.T, (int64_t)nbkv, zrows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (MAT && a.dpx) {  // Delta_i += sum_j P_ij dPx_ij
+        e = launch_mat_delta(a.p, a.dpx, a.delta, rows, a.T, stream);
+        if (e != hipSuccess) return e;
+    }
     const unsigned grid = runs > 0 ? (unsigned)(runs * nbkv) : (unsigned)n;
-    hipLaunchKernelGGL(attn_bwd_main_kernel<D>, dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v, a.dout,
-                       a.lse, a.delta, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb, nbkv, runs,
-                       a.scale, a.scale * kLog2e);
+    hipLaunchKernelGGL((attn_bwd_main_kernel<D, MAT>), dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v,
+                       a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
+                       nbkv, runs, a.scale, a.scale * kLog2e);
     return hipGetLastError();
 }
 
@@ -512,11 +533,22 @@ size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t T) { return (size_t)(
 
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream) {
     switch (a.D) {
-        case 8: return launch_bwd_d<8>(a, stream);
-        case 16: return launch_bwd_d<16>(a, stream);
-        case 32: return launch_bwd_d<32>(a, stream);
-        case 64: return launch_bwd_d<64>(a, stream);
-        case 128: return launch_bwd_d<128>(a, stream);
+        case 8: return launch_bwd_d<8, false>(a, stream);
+        case 16: return launch_bwd_d<16, false>(a, stream);
+        case 32: return launch_bwd_d<32, false>(a, stream);
+        case 64: return launch_bwd_d<64, false>(a, stream);
+        case 128: return launch_bwd_d<128, false>(a, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_materialized_bwd(const BwdArgs& a, hipStream_t stream) {
+    switch (a.D) {
+        case 8: return launch_bwd_d<8, true>(a, stream);
+        case 16: return launch_bwd_d<16, true>(a, stream);
+        case 32: return launch_bwd_d<32, true>(a, stream);
+        case 64: return launch_bwd_d<64, true>(a, stream);
+        case 128: return launch_bwd_d<128, true>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

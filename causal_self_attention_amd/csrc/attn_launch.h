@@ -25,6 +25,16 @@ struct BwdArgs {
     int64_t B, Hq, Hkv, T, D;
     float scale;
     int cu_count;
+    const float* p = nullptr;    // materialized variant: stored probabilities [B, Hq, T, T]
+    const float* dpx = nullptr;  // materialized variant: cotangent of P (may be NULL)
+};
+
+struct MatFwdArgs {
+    const float *q, *k, *v;
+    float *o, *lse, *p;  // p: [B, Hq, T, T]
+    int64_t B, Hq, Hkv, T, D;
+    float scale;
+    int cu_count;
 };
 
 struct DecodeArgs {
@@ -73,6 +83,10 @@ size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, in
 
 hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_materialized_fwd(const MatFwdArgs& a, hipStream_t stream);
+hipError_t launch_materialized_bwd(const BwdArgs& a, hipStream_t stream);  // a.p set
+hipError_t launch_mat_delta(const float* p, const float* dpx, float* delta, int64_t rows, int64_t T,
+                            hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 hipError_t launch_kv_release(const KvReleaseArgs& a, hipStream_t stream);

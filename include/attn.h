@@ -15,6 +15,12 @@
  *   attn_paged_decode  single-token decode over a paged K/V cache addressed
  *                      through per-sequence block tables ("Execution Backends
  *                      and the Python ABI", "Incremental attention").
+ *   attn_materialized_fwd  the materialized path: O, the row log-sum-exp and the
+ *   attn_materialized_bwd  probabilities P [B,H,T,T]; its VJP uses the stored P and
+ *                      accepts a cotangent of P ("Architecture", "Intentional
+ *                      limits"; "What the Metal slice does": the materialized
+ *                      path returns probabilities and context and keeps P for
+ *                      the VJPs; the probability diagnostic always takes it).
  *   attn_kv_append     the step before decode: lease pages from a device-resident
  *   attn_kv_release    free list and append each sequence's newest K/V rows, or
  *                      return a finished sequence's pages ("Architecture",
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 0x00010001u /* 1.1: major << 16 | minor */
+#define ATTN_ABI_VERSION 0x00010002u /* 1.2: major << 16 | minor */
 
 typedef int32_t attn_status;
 enum {
@@ -150,6 +156,38 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
                               int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
                               float scale, float* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Materialized causal attention: the same O and LSE as attn_causal_fwd, plus
+ *   p  [B, Hq, T, T] float32   p[b,h,i,j] = exp(scale q_i.k_j - lse[b,h,i]) for
+ *                              j <= i and 0 for j > i (every row sums to 1).
+ * o, p 16-byte aligned, lse 4-byte aligned; no output overlaps an input or
+ * another output.  B*Hq*T*T must stay below 2^40 elements.  Shapes and
+ * supported D as for attn_causal_fwd.
+ */
+attn_status attn_materialized_fwd(const float* q, const float* k, const float* v,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                                  float scale, float* o, float* lse, float* p, void* stream);
+
+/* Bytes of device workspace attn_materialized_bwd needs (0 when a size is invalid). */
+size_t attn_materialized_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D);
+
+/*
+ * VJP of the materialized path for L = sum(dout * O) + sum(dp * P), with the
+ * stored probabilities p (as written by attn_materialized_fwd; entries above the
+ * diagonal are taken as 0) and o the matching output:
+ *   dV = P^T dout,  dP = dout V^T + dp,  Delta_i = sum_j P_ij dP_ij,
+ *   dS = P (dP - Delta),  dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK, dV summed over the query heads of each key/value head.  dp
+ * [B,Hq,T,T] may be NULL (no loss on P).  Alignment, overlap and workspace rules
+ * as for attn_causal_bwd.  dQ accumulates with float atomics (last bits may vary);
+ * dK and dV are deterministic.
+ */
+attn_status attn_materialized_bwd(const float* q, const float* k, const float* v,
+                                  const float* o, const float* p, const float* dout, const float* dp,
+                                  int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,
+                                  float scale, float* dq, float* dk, float* dv,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Paged K/V cache maintenance: the step before attn_paged_decode.

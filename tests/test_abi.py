@@ -54,7 +54,7 @@ def test_header_is_c11_clean(tmp_path):
 
 
 def test_version_and_status_values(L):
-    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010001
+    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010002
     header = open(HEADER).read()
     for name in ("ATTN_OK", "ATTN_INVALID_ARGUMENT", "ATTN_UNSUPPORTED", "ATTN_WORKSPACE_TOO_SMALL",
                  "ATTN_DEVICE_ERROR"):
@@ -102,6 +102,23 @@ def _dec(L, S=2, Hq=4, Hkv=2, D=64, page=16, maxp=8, npages=16, scale=0.125, ws_
         ws_bytes = attn.attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page, maxp)
     return L.attn_paged_decode(p["q"], p["kp"], p["vp"], p["bt"], p["ctx"], S, Hq, Hkv, D, page, maxp, npages,
                                scale, p["o"], p["lse"], p["ws"], ws_bytes, None)
+
+
+def _matf(L, B=1, Hq=2, Hkv=2, T=16, D=8, scale=0.35, **ptrs):
+    names = ["q", "k", "v", "o", "lse", "p"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_materialized_fwd(p["q"], p["k"], p["v"], B, Hq, Hkv, T, D, scale, p["o"], p["lse"], p["p"], None)
+
+
+def _matb(L, B=1, Hq=2, Hkv=2, T=16, D=8, scale=0.35, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "o", "p", "dout", "dp", "dq", "dk", "dv", "ws"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = attn.attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
+    return L.attn_materialized_bwd(p["q"], p["k"], p["v"], p["o"], p["p"], p["dout"], p["dp"], B, Hq, Hkv, T, D,
+                                   scale, p["dq"], p["dk"], p["dv"], p["ws"], ws_bytes, None)
 
 
 def _app(L, S=3, Hkv=2, D=64, page=16, maxp=4, npages=8, **ptrs):
@@ -169,6 +186,20 @@ def test_decode_invalid_arguments(L):
     _expect(_dec(L, bt=ctypes.c_void_p(0x400000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
 
 
+def test_materialized_invalid_arguments(L):
+    _expect(_matf(L, p=None), attn.ATTN_INVALID_ARGUMENT, "'p' is NULL")
+    _expect(_matf(L, D=20), attn.ATTN_UNSUPPORTED, "D=20")
+    _expect(_matf(L, Hq=3, Hkv=2), attn.ATTN_INVALID_ARGUMENT, "Hq % Hkv")
+    _expect(_matf(L, p=_p(3)), attn.ATTN_INVALID_ARGUMENT, "overlap")  # p == o
+    _expect(_matf(L, B=1 << 10, Hq=1 << 10, T=1 << 10, D=8), attn.ATTN_INVALID_ARGUMENT, "2^40")
+    _expect(_matb(L, p=None), attn.ATTN_INVALID_ARGUMENT, "'p' is NULL")
+    _expect(_matb(L, ws_bytes=8), attn.ATTN_WORKSPACE_TOO_SMALL, "needs")
+    _expect(_matb(L, dq=_p(4)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'p'")
+    _expect(_matb(L, dv=_p(6)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'dp'")
+    _expect(_matb(L, dp=ctypes.c_void_p(0x700000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
+    _expect(_matb(L, scale=float("nan")), attn.ATTN_INVALID_ARGUMENT, "scale")
+
+
 def test_kv_invalid_arguments(L):
     _expect(_app(L, kn=None), attn.ATTN_INVALID_ARGUMENT, "'k_new' is NULL")
     _expect(_app(L, st=None), attn.ATTN_INVALID_ARGUMENT, "'kv_status' is NULL")
@@ -209,6 +240,9 @@ def test_valid_call_without_device_reports_device_error(L):
     _expect(_fwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_bwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_dec(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_matf(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_matb(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_matb(L, dp=None), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_app(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_rel(L), attn.ATTN_DEVICE_ERROR, "device")
 
