@@ -11,27 +11,35 @@
 // The operation is bound by the HBM read of the K/V pages, so the design aims
 // at streaming every byte once with plenty of loads in flight while keeping the
 // per-position instruction count low:
-//   1. attn_decode_split: one wave per (sequence, KV head, chunk of 256
-//      positions), 16 positions per step; the waves of a work-group are
-//      neighbouring KV heads of one chunk, so a page is read contiguously.  Both small contractions (scores of the
-//      G query heads that share the KV head, and the probability-weighted sum of
-//      V) run on fp32 MFMA, which is otherwise idle here; this takes the
-//      multiply-adds and their cross-lane reductions off the vector ALU, whose
-//      issue rate would otherwise bound the kernel below the HBM rate.  Each K
-//      and V row is read exactly once per KV head, as contiguous vectors.
-//      Positions past the context get score -inf and a zero V (a select, so a
-//      NaN in an unused slot cannot leak in).  Partial (m, l, o) go to the
-//      workspace.
-//   2. attn_decode_combine: per (sequence, query head), merges the chunks with
+//   1. attn_decode_split: the 16-position groups of all sequences, taken as one
+//      list, are dealt out in equal contiguous shares to a grid sized to the
+//      chip, so every CU streams about the same number of bytes however ragged
+//      the context lengths are; the waves of a work-group are neighbouring KV
+//      heads of the same positions, so a page is read contiguously.  Both small
+//      contractions (scores of the G query heads that share the KV head, and the
+//      probability-weighted sum of V) run on fp32 MFMA, which is otherwise idle
+//      here; this takes the multiply-adds and their cross-lane reductions off the
+//      vector ALU, whose issue rate would otherwise bound the kernel below the
+//      HBM rate.  Each K and V row is read exactly once per KV head, as
+//      contiguous vectors.  Positions past the context get score -inf and a zero
+//      V (a select, so a NaN in an unused slot cannot leak in).  One partial
+//      (m, l, o) per (work-group, sequence) it touches goes to the workspace.
+//   2. attn_decode_combine: per (sequence, query head), merges the partials with
 //      the log-sum-exp rule M = max m_c, L = sum 2^(m_c - M) l_c,
 //      O = sum 2^(m_c - M) o_c / L.
+// With at least one (sequence, KV head) pair per CU a single fused kernel takes a
+// whole pair per work-group instead.
+#include <algorithm>
+
 #include "attn_launch.h"
 #include "device_common.h"
 
 namespace attn {
 
-constexpr int kDecodeChunkTokens = 256;  // positions per wave
-constexpr int kDecodeWaves = 4;          // waves (KV heads) per work-group
+constexpr int kDecodeWaves = 4;          // waves (KV heads) per work-group of the split path
+constexpr int kDecodeWavesPerCu = 4;     // resident waves per CU the split grid aims at
+constexpr int kDecodeMaxWgs = 1024;      // bound on the split grid (sizes the workspace)
+constexpr int kDecodeDepth = 2;          // groups in flight per wave on the split path
 constexpr int kDecodeGroup = 16;         // positions per MFMA step
 constexpr float kLazyRescale = 8.f;      // log2 headroom before the running max is moved
 
@@ -67,6 +75,17 @@ __device__ __forceinline__ void load_vec(const float* __restrict__ p, float* x) 
     }
 }
 
+// Physical page of group j = lane of the list that starts at group g_first with
+// stride g_stride (ng groups; PS a power of two).  One unconditional load per lane:
+// lanes past the list re-read its last entry, and the page index is clamped to the
+// row and the id to the pool, so a broken table can never send a read out of bounds.
+__device__ __forceinline__ int decode_bt_lane(const int32_t* __restrict__ bt_row, int max_pages, int PS,
+                                              int num_pages, int g_first, int g_stride, int ng) {
+    const int lane = threadIdx.x & 63;
+    const int p = (16 * (g_first + g_stride * max(min(lane, ng - 1), 0))) >> __builtin_ctz(PS);
+    return min(max(bt_row[min(p, max_pages - 1)], 0), num_pages - 1);
+}
+
 // One wave works through a list of 16-position groups of one (sequence, KV head):
 // group j starts at position 16 * (g_first + g_stride * j), j < ng <= 64.  With
 // lane l = 16*g + i:
@@ -81,24 +100,23 @@ __device__ __forceinline__ void load_vec(const float* __restrict__ p, float* x) 
 // The VALU only scales, masks and exponentiates; the running max is moved (and
 // O, l rescaled) only when a score exceeds it by more than 2^8.  (m, l, acc)
 // carry over between calls, so a wave may take several lists in turn.
+//
+// The list's page ids come in bt_lane (decode_bt_lane: lane j holds group j's
+// physical page), fetched by the caller before anything else it loads, so no group
+// waits on a block-table read before it can issue its K/V loads.
 template <int D, int DEPTH, int NG_MAX>
 __device__ __forceinline__ void decode_groups(const float* __restrict__ Kp, const float* __restrict__ Vp,
-                                              const int32_t* __restrict__ bt_row, int Hkv, int kvh, int PS,
-                                              int num_pages, int ctx, int g_first, int g_stride, int ng,
-                                              const float (&qf)[DecTraits<D>::KSTEPS], float c2, float& m,
-                                              float& l, f32x4 (&acc)[DecTraits<D>::NDT]) {
+                                              int bt_lane, int Hkv, int kvh, int PS, int ctx, int g_first,
+                                              int g_stride, int ng, const float (&qf)[DecTraits<D>::KSTEPS],
+                                              float c2, float& m, float& l, f32x4 (&acc)[DecTraits<D>::NDT]) {
     using Tr = DecTraits<D>;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
-    // The list's page ids are fetched once, one per lane, before any K/V load, so
-    // no group waits on a block-table read before it can issue its loads.
-    int bt_lane = 0;
-    if (lane < ng) bt_lane = min(max(bt_row[(16 * (g_first + g_stride * lane)) / PS], 0), num_pages - 1);
     auto group_row = [&](int j) -> size_t {  // first pool row of group j
         const int p0 = 16 * (g_first + g_stride * j);
         const int phys = __builtin_amdgcn_readlane(bt_lane, j);
-        return ((size_t)phys * Hkv + kvh) * PS + (size_t)(p0 % PS);
+        return ((size_t)phys * Hkv + kvh) * PS + (size_t)(p0 & (PS - 1));
     };
 
     // Loads run DEPTH groups ahead through a register ring, issued unconditionally
@@ -191,7 +209,7 @@ __device__ __forceinline__ void decode_groups(const float* __restrict__ Kp, cons
     }
 }
 
-// B operand of S: Q^T[d][head li] for the G query heads of KV head kvh (zero columns past G)
+// B operand of S: Q^T[d][head li] for the G query heads of KV head kvh
 template <int D>
 __device__ __forceinline__ void decode_load_q(const float* __restrict__ Qd, int s, int Hq, int kvh, int G,
                                               float (&qf)[DecTraits<D>::KSTEPS]) {
@@ -199,80 +217,235 @@ __device__ __forceinline__ void decode_load_q(const float* __restrict__ Qd, int 
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
-    const float* qrow = Qd + ((size_t)s * Hq + (size_t)kvh * G + li) * D;
+    // Columns past G repeat the group's first query head: their scores and outputs
+    // are formed but never stored, and the loads need no branch or select, so nothing
+    // waits on them before the block-table loads are issued.
+    const float* qrow = Qd + ((size_t)s * Hq + (size_t)kvh * G + (li < G ? li : 0)) * D;
 #pragma unroll
-    for (int u = 0; u < Tr::KSTEPS / Tr::KW; ++u) {
-        float x[Tr::KW];
-        if (li < G) load_vec<Tr::KW>(qrow + 4 * Tr::KW * u + Tr::KW * g, x);
-        else {
-#pragma unroll
-            for (int j = 0; j < Tr::KW; ++j) x[j] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < Tr::KW; ++j) qf[Tr::KW * u + j] = x[j];
-    }
+    for (int u = 0; u < Tr::KSTEPS / Tr::KW; ++u) load_vec<Tr::KW>(qrow + 4 * Tr::KW * u + Tr::KW * g, &qf[Tr::KW * u]);
 }
 
-// Split path, one wave per (sequence, KV head, chunk of 256 positions); the waves
-// of a work-group are neighbouring KV heads of one chunk, so a page is read
-// contiguously.  Partials (m, l, o) go to the workspace.
-template <int D>
+// Inclusive prefix sum over the 64 lanes of a wave on DPP moves (no LDS): shifted
+// adds inside each 16-lane row (a lane whose source is outside its row adds 0), then
+// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the total of
+// rows 0-1 into rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_add(int x) {
+    return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x = dpp_add<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_add<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_add<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_add<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// The split path's partition, computed by every wave on its own from the
+// sequence lengths (no LDS, no barrier): lane l of chunk c stands for sequence
+// s = 64c + l (S <= 64 * NCH) and holds P_{s+1}, the number of 16-position groups
+// of sequences 0..s.  Lengths are clamped to the block table's capacity (and a
+// negative one taken as 0), so a broken length can give wrong numbers but never an
+// out-of-bounds read.
+constexpr int kDecodeScanChunks = 4;  // largest NCH: up to 256 sequences on the split path
+
+template <int NCH>
+struct DecodePartition {
+    int incl[NCH];  // P_{s+1} at lane s % 64 of chunk s / 64
+    int len[NCH];   // clamped length of sequence s, same places
+    int total;      // P_S
+    int nact;       // active work-groups: min(nwg, total)
+
+    // Two steps, so that other loads can be issued between them: load() issues the
+    // length loads (all chunks at once), scan() waits for them and forms the sums.
+    __device__ __forceinline__ void load(const int32_t* __restrict__ CTX, int S) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) len[c] = CTX[min(64 * c + lane, S - 1)];  // unconditional loads
+    }
+    __device__ __forceinline__ void scan(int S, int cap, int nwg) {
+        const int lane = threadIdx.x & 63;
+        int carry = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            len[c] = 64 * c + lane < S ? min(max(len[c], 0), cap) : 0;
+            incl[c] = carry + wave_incl_scan((len[c] + 15) / 16);
+            carry = __builtin_amdgcn_readlane(incl[c], 63);
+        }
+        total = wave_uniform(carry);
+        nact = min(nwg, total);
+    }
+    // value of a per-sequence register at sequence s (wave-uniform s < 64 * NCH)
+    __device__ __forceinline__ static int at(const int (&v)[NCH], int s) {
+        int x = v[0];
+#pragma unroll
+        for (int c = 1; c < NCH; ++c) x = (s >> 6) == c ? v[c] : x;
+        return __builtin_amdgcn_readlane(x, s & 63);
+    }
+    __device__ __forceinline__ int start(int s) const { return s == 0 ? 0 : at(incl, s - 1); }  // P_s
+    __device__ __forceinline__ int end(int s) const { return at(incl, s); }                     // P_{s+1}
+    __device__ __forceinline__ int length(int s) const { return at(len, s); }
+    // the work-group owning group u: work-group w takes groups [w N / n, (w+1) N / n)
+    __device__ __forceinline__ int owner(int u) const { return (int)((((int64_t)u + 1) * nact - 1) / total); }
+    // sequences that end at or before group u
+    __device__ __forceinline__ int ended_by(int u, int S) const {
+        const int lane = threadIdx.x & 63;
+        int n = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) n += __popcll(__ballot(64 * c + lane < S && incl[c] <= u));
+        return n;
+    }
+};
+
+// Balanced split path (fewer (sequence, KV head) pairs than CUs).  The 16-position
+// groups of all sequences form one list, sequence after sequence (N groups in all);
+// work-group w of n = min(nwg, N) takes groups [w N / n, (w+1) N / n), so every
+// work-group streams the same number of K/V bytes to within one group, whatever the
+// mix of context lengths.  A range may start or end inside a sequence and may cover
+// several: for each sequence it touches the work-group writes one partial (m, l, o) of
+// every query head of its KV heads, into slot k = w - owner(first group of the
+// sequence) of that sequence (k < kcap: a sequence spans at most min(n, its group
+// count) work-groups).  The waves of a work-group are neighbouring KV heads of the
+// same positions, so a page is read contiguously.
+template <int D, int DEPTH, int NCH>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     const float* __restrict__ Qd, const float* __restrict__ Kp, const float* __restrict__ Vp,
     const int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, float* __restrict__ Po,
-    float* __restrict__ Pm, float* __restrict__ Pl, int Hq, int Hkv, int PS, int max_pages, int num_pages,
-    int max_chunks, float c2 /* scale * log2(e) */) {
+    float* __restrict__ Pm, float* __restrict__ Pl, int32_t* __restrict__ Cnt, int S, int Hq, int Hkv, int PS,
+    int max_pages, int num_pages, int nwg, int kcap, float c2 /* scale * log2(e) */) {
     using Tr = DecTraits<D>;
-    const int s = blockIdx.z;
     const int w = wave_uniform(threadIdx.x >> 6);
-    const int kvh = blockIdx.y * kDecodeWaves + w;
-    if (kvh >= Hkv) return;  // wave-uniform
+    const int kvh = blockIdx.y * (blockDim.x >> 6) + w;
+    if (kvh >= Hkv) return;  // wave-uniform; the kernel has no barrier
+    DecodePartition<NCH> pt;
+    pt.load(CTX, S);
+    pt.scan(S, PS * max_pages, nwg);
+    const int wg = blockIdx.x;
+    if (wg >= pt.nact) return;
+    const int u_lo = wave_uniform((int)(((int64_t)wg * pt.total) / pt.nact));
+    const int u_hi = wave_uniform((int)(((int64_t)(wg + 1) * pt.total) / pt.nact));
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
     const int G = Hq / Hkv;
-    const int chunk = blockIdx.x;
-    // a length past the block table's capacity is clamped, so a broken length can
-    // give wrong numbers but never an out-of-bounds read
-    const int ctx = min(CTX[s], PS * max_pages);
-    const int pos_begin = chunk * kDecodeChunkTokens;
-    if (pos_begin >= ctx) return;  // wave-uniform: this chunk is past the sequence
-    const int pos_end = min(pos_begin + kDecodeChunkTokens, ctx);
+    for (int s = wave_uniform(pt.ended_by(u_lo, S)); s < S; ++s) {
+        const int ps = wave_uniform(pt.start(s)), pe = wave_uniform(pt.end(s));
+        if (ps >= u_hi) break;
+        const int a = max(ps, u_lo), e = min(pe, u_hi);
+        if (a >= e) continue;  // a sequence without positions
+        const int ctx = wave_uniform(pt.length(s));
+        const int32_t* bt_row = BT + (size_t)s * max_pages;
+        int bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, a - ps, 1, min(64, e - a));
+        float qf[Tr::KSTEPS];
+        decode_load_q<D>(Qd, s, Hq, kvh, G, qf);
+        float m = -INFINITY;  // running max of head li (log2 units), same in its four lanes
+        float l = 0.f;        // this lane's share of head li's running sum
+        f32x4 acc[Tr::NDT];   // O[head 4g + r][d = NDT*li + dt]
+#pragma unroll
+        for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j0 = a; j0 < e; j0 += 64) {
+            decode_groups<D, DEPTH, 0>(Kp, Vp, bt, Hkv, kvh, PS, ctx, j0 - ps, 1, min(64, e - j0), qf, c2, m, l, acc);
+            bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, j0 + 64 - ps, 1, min(64, e - j0 - 64));
+        }
 
-    float qf[Tr::KSTEPS];
-    decode_load_q<D>(Qd, s, Hq, kvh, G, qf);
-    float m = -INFINITY;  // running max of head li (log2 units), same in its four lanes
-    float l = 0.f;        // this lane's share of head li's running sum
-    f32x4 acc[Tr::NDT];   // O[head 4g + r][d = NDT*li + dt]
+        // partial: head h = 4g + r lives in lanes (g, *), register r; head li's l in lanes (*, li)
+        const float lt = rows4_sum(l);
+        const int k = wg - pt.owner(ps);  // this partial's slot among the sequence's
+        if (k == 0 && kvh == blockIdx.y * (blockDim.x >> 6) && lane == 0)  // one writer per (sequence, column)
+            Cnt[(size_t)blockIdx.y * S + s] = pe > ps ? pt.owner(pe - 1) - pt.owner(ps) + 1 : 0;
+        const size_t slot = (size_t)s * kcap + k;
+        const size_t hb = slot * Hq + (size_t)kvh * G;  // row of query head kvh * G
 #pragma unroll
-    for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    decode_groups<D, 2, kDecodeChunkTokens / 16>(Kp, Vp, BT + (size_t)s * max_pages, Hkv, kvh, PS, num_pages, ctx,
-                                                 pos_begin / 16, 1,
-                                                 (pos_end - pos_begin + 15) / 16, qf, c2, m, l, acc);
-
-    // partials: head h = 4g + r lives in lanes (g, *), register r; head li's l in lanes (*, li)
-    const float lt = rows4_sum(l);
-    const size_t pbase = ((size_t)s * Hkv + kvh) * max_chunks + chunk;
+        for (int r = 0; r < 4; ++r) {
+            const int h = 4 * g + r;
+            if (h < G) {
+                float* dst = Po + (hb + h) * D + Tr::NDT * li;
+                if constexpr (Tr::NDT % 4 == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * g + r;
-        if (h < G) {
-            float* dst = Po + (pbase * G + h) * D + Tr::NDT * li;
-            if constexpr (Tr::NDT % 4 == 0) {
+                    for (int dt = 0; dt < Tr::NDT; dt += 4)
+                        *(f32x4*)(dst + dt) = f32x4{acc[dt][r], acc[dt + 1][r], acc[dt + 2][r], acc[dt + 3][r]};
+                } else {
 #pragma unroll
-                for (int dt = 0; dt < Tr::NDT; dt += 4)
-                    *(f32x4*)(dst + dt) = f32x4{acc[dt][r], acc[dt + 1][r], acc[dt + 2][r], acc[dt + 3][r]};
-            } else {
-#pragma unroll
-                for (int dt = 0; dt < Tr::NDT; ++dt)
-                    if (D >= 16 || li < D) dst[dt] = acc[dt][r];
+                    for (int dt = 0; dt < Tr::NDT; ++dt)
+                        if (D >= 16 || li < D) dst[dt] = acc[dt][r];
+                }
             }
         }
+        if (g == 0 && li < G) {
+            Pm[hb + li] = m;
+            Pl[hb + li] = lt;
+        }
     }
-    if (g == 0 && li < G) {
-        Pm[pbase * G + li] = m;
-        Pl[pbase * G + li] = lt;
+}
+
+// One wave per (sequence, query head) merges the sequence's partials with the
+// log-sum-exp rule M = max m_c, L = sum 2^(m_c - M) l_c, O = sum 2^(m_c - M) o_c / L,
+// 64 partials per pass with a running (M, L, o): lane c holds partial c's statistics,
+// the weight of partial c reaches every lane by a lane read, and the lanes sweep the
+// head dim (dims lane and lane + 64).  The sequence's partials sit in fixed slots, so
+// the first pass's loads go out together with the load of their count; slots past the
+// count are masked by selects.
+constexpr int kCombineBatch = 16;  // partial rows loaded together
+
+__global__ __launch_bounds__(64) void attn_decode_combine_kernel(
+    const float* __restrict__ Po, const float* __restrict__ Pm, const float* __restrict__ Pl,
+    const int32_t* __restrict__ Cnt, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int Hkv, int D,
+    int kcap) {
+    const int lane = threadIdx.x;
+    const int s = blockIdx.x / Hq;
+    const int h = blockIdx.x % Hq;
+    const int col = h / (Hq / Hkv) / kDecodeWaves;  // column of KV heads that wrote this head
+    const size_t first = (size_t)s * kcap;
+    const bool d0 = lane < D, d1 = lane + 64 < D;
+    const int n_ld = Cnt[(size_t)col * S + s];
+    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+    for (int c0 = 0; c0 < kcap; c0 += 64) {
+        const int c = c0 + lane;
+        const int cn = min(64, kcap - c0);  // slots of this pass
+        const size_t row = (first + c0 + min(lane, cn - 1)) * Hq + h;
+        const float pm_ld = Pm[row], pl_ld = Pl[row];  // unconditional loads, masked below
+        float x0[kCombineBatch], x1[kCombineBatch];
+        auto load = [&](int cb) {
+#pragma unroll
+            for (int j = 0; j < kCombineBatch; ++j) {
+                const float* src = Po + ((first + c0 + min(cb + j, cn - 1)) * Hq + h) * D;
+                const float y0 = src[min(lane, D - 1)], y1 = src[min(lane + 64, D - 1)];
+                x0[j] = d0 ? y0 : 0.f;
+                x1[j] = d1 ? y1 : 0.f;
+            }
+        };
+        load(0);
+        const int n = wave_uniform(n_ld);  // the sequence's partial count
+        if (c0 >= n) break;                // wave-uniform
+        const bool valid = c < n;
+        const float pm = valid ? pm_ld : -INFINITY;
+        const float m_new = fmaxf(M, wave_max(pm));  // finite: partial c0 exists
+        const float keep = exp2_hw(M - m_new);        // 0 on the first pass
+        const float wl = valid ? exp2_hw(pm - m_new) : 0.f;
+        L = L * keep + wave_sum(valid ? wl * pl_ld : 0.f);
+        acc0 *= keep;
+        acc1 *= keep;
+        M = m_new;
+        const int cv = min(64, n - c0);  // valid partials of this pass
+        for (int cb = 0; cb < cv; cb += kCombineBatch) {
+            if (cb > 0) load(cb);
+#pragma unroll
+            for (int j = 0; j < kCombineBatch; ++j) {
+                const float wj = __builtin_amdgcn_readlane(__float_as_int(wl), min(cb + j, 63));
+                const bool ok = cb + j < cv;
+                acc0 += ok ? __int_as_float(wj) * x0[j] : 0.f;
+                acc1 += ok ? __int_as_float(wj) * x1[j] : 0.f;
+            }
+        }
+        if (c0 + 64 >= n) break;  // wave-uniform: no further pass
     }
+    const float inv = 1.f / L;
+    float* dst = O + ((size_t)s * Hq + h) * D;
+    if (d0) dst[lane] = acc0 * inv;
+    if (d1) dst[lane + 64] = acc1 * inv;
+    if (LSE && lane == 0) LSE[(size_t)s * Hq + h] = (M + log2_hw(L)) * kLn2;
 }
 
 // Fused path, one work-group of NW waves per (sequence, KV head): wave w takes the
@@ -303,6 +476,9 @@ __global__ __launch_bounds__(64 * fused_waves<D>()) void attn_decode_fused_kerne
     const int ctx = min(CTX[s], PS * max_pages);  // clamped as in the split path
     const int ngroups = (ctx + 15) / 16;
 
+    const int mine = w < ngroups ? (ngroups - w + NW - 1) / NW : 0;  // this wave's groups
+    const int32_t* bt_row = BT + (size_t)s * max_pages;
+    int bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, w, NW, min(64, mine));
     float qf[Tr::KSTEPS];
     decode_load_q<D>(Qd, s, Hq, kvh, G, qf);
     float m = -INFINITY;
@@ -310,10 +486,10 @@ __global__ __launch_bounds__(64 * fused_waves<D>()) void attn_decode_fused_kerne
     f32x4 acc[Tr::NDT];
 #pragma unroll
     for (int dt = 0; dt < Tr::NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int mine = w < ngroups ? (ngroups - w + NW - 1) / NW : 0;  // this wave's groups
-    for (int j0 = 0; j0 < mine; j0 += 64)
-        decode_groups<D, 2, 0>(Kp, Vp, BT + (size_t)s * max_pages, Hkv, kvh, PS, num_pages, ctx,
-                            w + NW * j0, NW, min(64, mine - j0), qf, c2, m, l, acc);
+    for (int j0 = 0; j0 < mine; j0 += 64) {
+        decode_groups<D, 2, 0>(Kp, Vp, bt, Hkv, kvh, PS, ctx, w + NW * j0, NW, min(64, mine - j0), qf, c2, m, l, acc);
+        bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, w + NW * (j0 + 64), NW, min(64, mine - j0 - 64));
+    }
 
     // this wave's partial: O[head 4g + r][d] in registers, head li's max and sum in lanes (*, li)
     const float lt = rows4_sum(l);
@@ -347,99 +523,31 @@ __global__ __launch_bounds__(64 * fused_waves<D>()) void attn_decode_fused_kerne
     }
 }
 
-// One wave per (sequence, query head) merges the chunks' partials, 64 chunks per
-// pass with a running (M, L, o): lane c holds chunk c's statistics, the weight of
-// chunk c reaches every lane by a lane read, and the lanes sweep the head dim
-// (dims lane and lane + 64).  The loads of the first pass go out before the
-// context length is known (the workspace holds max_chunks slots; slots past the
-// sequence's chunk count are masked by selects), so the kernel waits on about one
-// memory round trip instead of three.
-constexpr int kCombineBatch = 16;  // chunks whose partial rows are loaded together
-
-__global__ __launch_bounds__(64) void attn_decode_combine_kernel(
-    const float* __restrict__ Po, const float* __restrict__ Pm, const float* __restrict__ Pl,
-    const int32_t* __restrict__ CTX, float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int D,
-    int max_chunks) {
-    const int lane = threadIdx.x;
-    const int s = blockIdx.x / Hq;
-    const int h = blockIdx.x % Hq;
-    const int G = Hq / Hkv;
-    const int kvh = h / G;
-    const int hh = h % G;
-    const size_t base = ((size_t)s * Hkv + kvh) * max_chunks;
-    const bool d0 = lane < D, d1 = lane + 64 < D;
-    const int ctx = CTX[s];
-    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int c0 = 0; c0 < max_chunks; c0 += 64) {
-        const int c = c0 + lane;
-        const bool have = c < max_chunks;
-        const float pm_raw = have ? Pm[(base + c) * G + hh] : -INFINITY;
-        const float pl_raw = have ? Pl[(base + c) * G + hh] : 0.f;
-        const int cn = min(64, max_chunks - c0);
-        float x0[kCombineBatch], x1[kCombineBatch];
-#pragma unroll
-        for (int j = 0; j < kCombineBatch; ++j) {  // first batch of partial rows, issued early
-            const float* src = Po + ((base + c0 + min(j, cn - 1)) * G + hh) * D;
-            x0[j] = d0 ? src[lane] : 0.f;
-            x1[j] = d1 ? src[lane + 64] : 0.f;
-        }
-        const int nch = (min(ctx, max_chunks * kDecodeChunkTokens) + kDecodeChunkTokens - 1) / kDecodeChunkTokens;
-        if (c0 >= nch) break;  // wave-uniform
-        const bool valid = c < nch;
-        const float pm = valid ? pm_raw : -INFINITY;
-        const float m_new = fmaxf(M, wave_max(pm));  // finite: chunk c0 is valid
-        const float keep = exp2_hw(M - m_new);        // 0 on the first pass
-        const float wl = valid ? exp2_hw(pm - m_new) : 0.f;
-        L = L * keep + wave_sum(valid ? wl * pl_raw : 0.f);
-        acc0 *= keep;
-        acc1 *= keep;
-        M = m_new;
-        const int cv = min(64, nch - c0);  // valid chunks of this pass
-        for (int cb = 0; cb < cv; cb += kCombineBatch) {
-            if (cb > 0) {
-#pragma unroll
-                for (int j = 0; j < kCombineBatch; ++j) {
-                    const float* src = Po + ((base + c0 + min(cb + j, cn - 1)) * G + hh) * D;
-                    x0[j] = d0 ? src[lane] : 0.f;
-                    x1[j] = d1 ? src[lane + 64] : 0.f;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < kCombineBatch; ++j) {
-                const float wj = __builtin_amdgcn_readlane(__float_as_int(wl), min(cb + j, 63));
-                const bool ok = cb + j < cv;
-                acc0 += ok ? __int_as_float(wj) * x0[j] : 0.f;
-                acc1 += ok ? __int_as_float(wj) * x1[j] : 0.f;
-            }
-        }
-    }
-    const float inv = 1.f / L;
-    float* dst = O + ((size_t)s * Hq + h) * D;
-    if (d0) dst[lane] = acc0 * inv;
-    if (d1) dst[lane + 64] = acc1 * inv;
-    if (LSE && lane == 0) LSE[(size_t)s * Hq + h] = (M + log2_hw(L)) * kLn2;
-}
-
-static int64_t decode_max_chunks(int64_t page_size, int64_t max_pages) {
-    return (page_size * max_pages + kDecodeChunkTokens - 1) / kDecodeChunkTokens;
-}
-
 bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group) {
     const bool d_ok = D == 8 || D == 16 || D == 32 || D == 64 || D == 128;
     const bool p_ok = page_size == 16 || page_size == 32 || page_size == 64;
     return d_ok && p_ok && group >= 1 && group <= 16;
 }
 
+// Partial slots per sequence on the split path: a sequence spans at most as many
+// work-groups as it has 16-position groups, and at most the grid.
+static int64_t decode_slots_per_seq(int64_t page_size, int64_t max_pages) {
+    return std::min<int64_t>(kDecodeMaxWgs, (page_size * max_pages + 15) / 16);
+}
+
+// Workspace (floats): o [S][slots][Hq][D], then m and l [S][slots][Hq], then the
+// partial counts [ceil(Hkv / 4)][S] (int32).
 size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages) {
-    (void)Hkv;
-    const int64_t nch = decode_max_chunks(page_size, max_pages);
-    return (size_t)(S * Hq * nch * (D + 2));
+    return (size_t)(S * decode_slots_per_seq(page_size, max_pages) * Hq * (D + 2) +
+                    (Hkv + kDecodeWaves - 1) / kDecodeWaves * S);
 }
+
+bool decode_split_supported(int64_t S) { return S <= 64 * kDecodeScanChunks; }
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
-    if (a.S * a.Hkv >= a.cu_count) {
+    if (a.S * a.Hkv >= a.cu_count || !decode_split_supported(a.S)) {
         // At least one (sequence, KV head) pair per CU: one fused kernel.
         hipLaunchKernelGGL((attn_decode_fused_kernel<D>), dim3((unsigned)a.Hkv, (unsigned)a.S),
                            dim3(64 * fused_waves<D>()), 0, stream, a.q, a.k_pool, a.v_pool, a.block_table,
@@ -447,19 +555,25 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                            (int)a.max_pages, (int)a.num_pages, a.scale * kLog2e);
         return hipGetLastError();
     }
-    // Few pairs: split every context into chunks over the whole chip, then combine.
-    const int64_t nch = decode_max_chunks(a.page_size, a.max_pages);
+    // Few pairs: the positions of all sequences in equal shares over the whole chip, then the merge.
+    const int wpw = (int)std::min<int64_t>(a.Hkv, kDecodeWaves);  // waves (KV heads) per work-group
+    const int gy = (int)((a.Hkv + wpw - 1) / wpw);
+    const int nwg = (int)std::max<int64_t>(
+        1, std::min<int64_t>(kDecodeMaxWgs, (int64_t)kDecodeWavesPerCu * a.cu_count / (wpw * gy)));
+    const int kcap = (int)decode_slots_per_seq(a.page_size, a.max_pages);
     float* Po = a.partial;
-    float* Pm = Po + (size_t)(a.S * a.Hq * nch * D);
-    float* Pl = Pm + (size_t)(a.S * a.Hq * nch);
-    const dim3 grid((unsigned)nch, (unsigned)((a.Hkv + kDecodeWaves - 1) / kDecodeWaves), (unsigned)a.S);
-    hipLaunchKernelGGL((attn_decode_split_kernel<D>), grid, dim3(64 * kDecodeWaves), 0, stream, a.q, a.k_pool,
-                       a.v_pool, a.block_table, a.context_lens, Po, Pm, Pl, (int)a.Hq, (int)a.Hkv,
-                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages, (int)nch, a.scale * kLog2e);
+    float* Pm = Po + (size_t)(a.S * kcap * a.Hq * D);
+    float* Pl = Pm + (size_t)(a.S * kcap * a.Hq);
+    int32_t* Cnt = (int32_t*)(Pl + (size_t)(a.S * kcap * a.Hq));
+    auto split = a.S <= 64 ? attn_decode_split_kernel<D, kDecodeDepth, 1>
+                           : attn_decode_split_kernel<D, kDecodeDepth, kDecodeScanChunks>;
+    hipLaunchKernelGGL(split, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), 0, stream, a.q, a.k_pool, a.v_pool,
+                       a.block_table, a.context_lens, Po, Pm, Pl, Cnt, (int)a.S, (int)a.Hq, (int)a.Hkv,
+                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, kcap, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream,
-                       Po, Pm, Pl, a.context_lens, a.o, a.lse, (int)a.Hq, (int)a.Hkv, D, (int)nch);
+    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,
+                       Cnt, a.o, a.lse, (int)a.S, (int)a.Hq, (int)a.Hkv, D, kcap);
     return hipGetLastError();
 }
 

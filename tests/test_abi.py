@@ -67,11 +67,15 @@ def test_workspace_queries(L):
     assert attn.attn_causal_bwd_workspace_bytes(1, 2, 2, 16, 8) == 256  # rounded up to 256
     assert attn.attn_causal_bwd_workspace_bytes(1, 3, 2, 16, 8) == 0    # Hq % Hkv != 0
     assert attn.attn_causal_bwd_workspace_bytes(0, 2, 2, 16, 8) == 0
-    ws = attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 256)
-    # partial (m, l, o[D]) records per sequence, query head and chunk, 256-byte rounded
-    assert ws % 256 == 0 and ws >= 32 * 16 * (64 + 2) * 4
-    assert attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 512) > ws
-    assert attn.attn_paged_decode_workspace_bytes(32, 16, 4, 64, 16, 1) >= 32 * 16 * (64 + 2) * 4
+    # partial (m, l, o[D]) records per sequence and query head for min(1024, capacity / 16)
+    # slots (a sequence spans at most that many work-groups) and one int per sequence and
+    # column of 4 KV heads, 256-byte rounded
+    def expect(S, Hq, Hkv, D, ps, maxp):
+        b = S * min(1024, -(-ps * maxp // 16)) * Hq * (D + 2) * 4 + -(-Hkv // 4) * S * 4
+        return -(-b // 256) * 256
+    for args in ((32, 16, 4, 64, 16, 256), (32, 16, 4, 64, 16, 512), (32, 16, 4, 64, 16, 1),
+                 (32, 16, 4, 64, 16, 100000), (3, 8, 8, 32, 64, 7), (1, 1, 1, 8, 16, 1)):
+        assert attn.attn_paged_decode_workspace_bytes(*args) == expect(*args), args
     assert attn.attn_paged_decode_workspace_bytes(32, 16, 5, 64, 16, 256) == 0
 
 

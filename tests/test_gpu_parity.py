@@ -382,6 +382,22 @@ def test_decode_long_context(dev, orc, path):
     assert rel_err(lse, rlse) <= TOL_DECODE
 
 
+def test_decode_split_many_sequences(dev, orc):
+    """More sequences than one wave's lanes on the split path (the partition's prefix
+    sums carry across 64-sequence chunks), with empty-looking short ones mixed in."""
+    Hkv, G, D, ps = 1, 4, 64, 16
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    S = min(200, cus - 1)
+    announce(f"decode split S={S}")
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=300,
+                               max_pages=math.ceil(300 / ps), seed=91)
+    d["context_lens"][::7] = 1
+    o, lse = _decode(d, dev)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE
+
+
 def test_decode_matches_causal_last_row(dev):
     """Decode over a contiguous sequence equals the causal forward's last row."""
     announce("decode vs causal last row")
