@@ -11,8 +11,9 @@ Printed: one JSON line.  `value` is the causal forward+backward rate in
 algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
 QK^T recompute, dV, dP, dK, dQ backward) over the summed event times of the two
 calls; the decode rate (algorithmic HBM bytes per call / call time), the
-8192-token grouped-query forward and backward and the latency of a K/V append
-(the step before decode) are reported beside it.  Each decode call
+8192-token grouped-query forward and backward, the materialized path, a batched
+paged prefill of a ragged 8-sequence batch and the latency of a K/V append (the
+step before decode) are reported beside it.  Each decode call
 reads a different one of several pool replicas so the 256 MB last-level cache
 cannot serve a repeated pool.
 
@@ -45,6 +46,7 @@ BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "1f5e43d90a40d304"
 CAUSAL = "mha_b4_h8_t1024_d64"
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"
 DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
+PREFILL = "paged_prefill_s8_hq16_hkv4_d64_p16"
 
 
 def causal_flops(B, Hq, T, D):
@@ -271,6 +273,31 @@ def main():
     app_us = statistics.median(a.elapsed_time(b) for a, b in aev) * 1e3
     app_bytes = 2 * 2 * S_ * Hkv_ * D_ * 4  # new K and V rows read once and written once
 
+    # batched prefill over the paged cache: the ragged 8-sequence workload (new tokens
+    # already in the cache), O + LSE; 4*d flops per (new token, visible position, head)
+    pcfg = si.PREFILL_WORKLOADS[PREFILL]
+    ph = si.prefill_workload(PREFILL)
+    pdev = {k: ph[k].to(dev) for k in ("q", "k_pool", "v_pool", "block_table", "context_lens", "token_start")}
+    po = torch.empty_like(pdev["q"])
+    plse = torch.empty((ph["N"], pcfg["Hq"]), device=dev)
+    pts, pctx = ph["token_start"].tolist(), ph["context_lens"].tolist()
+    p_pairs = 0
+    for s_ in range(pcfg["S"]):
+        n_ = pts[s_ + 1] - pts[s_]
+        c_ = pctx[s_]
+        p_pairs += sum(c_ - n_ + j + 1 for j in range(n_))
+    p_flops = 4 * pcfg["D"] * pcfg["Hq"] * p_pairs
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
+    torch.cuda.synchronize()
+    for a, b in pev:
+        a.record(stream)
+        attn.attn_paged_prefill(pdev["q"], pdev["k_pool"], pdev["v_pool"], pdev["block_table"],
+                                pdev["context_lens"], pdev["token_start"], o=po, lse=plse, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    pre_us = statistics.median(a.elapsed_time(b) for a, b in pev[2:]) * 1e3
+    del pdev, po, plse
+
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -328,6 +355,11 @@ def main():
             "workload": CAUSAL, "fwd_us_median": round(m_fwd_us, 2), "bwd_us_median": round(m_bwd_us, 2),
             "p_bytes": p_bytes, "fwd_p_store_gbps": round(p_bytes / (m_fwd_us * 1e-6) / 1e9, 1),
             "bwd_tflops": round(bwd_flops / (m_bwd_us * 1e-6) / 1e12, 3),
+        },
+        "paged_prefill": {
+            "workload": PREFILL, "new_tokens": ph["N"], "us_median": round(pre_us, 2), "flops": p_flops,
+            "tflops": round(p_flops / (pre_us * 1e-6) / 1e12, 3),
+            "frac_of_fp32_mfma_peak": round(p_flops / (pre_us * 1e-6) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         },
         "kv_append": {
             "us_median": round(app_us, 2), "bytes_per_call": app_bytes,

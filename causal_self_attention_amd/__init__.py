@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     attn_causal_bwd_workspace_bytes,
     attn_causal_fwd,
     attn_kv_append,
+    attn_kv_append_tokens,
     attn_kv_release,
     attn_last_error,
     attn_materialized_bwd,
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
     attn_materialized_fwd,
     attn_paged_decode,
     attn_paged_decode_workspace_bytes,
+    attn_paged_prefill,
     lib,
     library_path,
 )

@@ -24,7 +24,7 @@ ATTN_INVALID_ARGUMENT = 1
 ATTN_UNSUPPORTED = 2
 ATTN_WORKSPACE_TOO_SMALL = 3
 ATTN_DEVICE_ERROR = 4
-ATTN_ABI_VERSION = 0x00010002
+ATTN_ABI_VERSION = 0x00010003
 
 ATTN_KV_OK = 0
 ATTN_KV_POOL_EXHAUSTED = 1
@@ -62,6 +62,10 @@ SIGNATURES = {
     "attn_kv_append": (_st, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _vp]),
     "attn_kv_release": (_st, [_vp, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "attn_kv_append_tokens": (_st, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp]),
+    "attn_paged_prefill": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                 _f, _vp, _vp, _vp]),
 }
 
 
@@ -291,6 +295,9 @@ class PagedKvCache:
     def append(self, k_new, v_new, stream=None):
         attn_kv_append(k_new, v_new, self, stream=stream)
 
+    def append_tokens(self, k_new, v_new, token_start, stream=None):
+        attn_kv_append_tokens(k_new, v_new, token_start, self, stream=stream)
+
     def release(self, seq_ids, stream=None):
         attn_kv_release(seq_ids, self, stream=stream)
 
@@ -313,6 +320,56 @@ def attn_kv_append(k_new, v_new, cache, stream=None):
                                 _dev(c.free_pages, "free_pages", torch.int32),
                                 _dev(c.free_count, "free_count", torch.int32),
                                 _dev(c.kv_status, "kv_status", torch.int32), _stream_ptr(stream, dev)))
+
+
+def attn_kv_append_tokens(k_new, v_new, token_start, cache, stream=None):
+    """Lease pages where needed and append, to each sequence s, the rows
+    token_start[s] .. token_start[s+1]-1 of k_new, v_new [N, Hkv, D] (token_start: int32
+    device tensor [S + 1]; async, the outcome lands in cache.kv_status)."""
+    c = cache
+    dev = _same_device(k_new, v_new, token_start, c.k_pool)
+    if k_new.dim() != 3 or k_new.shape[1:] != (c.Hkv, c.D) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [N, {c.Hkv}, {c.D}], got {tuple(k_new.shape)}")
+    if token_start.shape != (c.S + 1,):
+        raise ValueError(f"token_start must be [{c.S + 1}]")
+    N = k_new.shape[0]
+    kp = _dev(k_new, "k_new") if N > 0 else ctypes.c_void_p(0)
+    vp = _dev(v_new, "v_new") if N > 0 else ctypes.c_void_p(0)
+    _check(lib().attn_kv_append_tokens(kp, vp, _dev(token_start, "token_start", torch.int32), c.S, N, c.Hkv, c.D,
+                                       c.page_size, c.max_pages, c.num_pages, _dev(c.k_pool, "k_pool"),
+                                       _dev(c.v_pool, "v_pool"), _dev(c.block_table, "block_table", torch.int32),
+                                       _dev(c.context_lens, "context_lens", torch.int32),
+                                       _dev(c.free_pages, "free_pages", torch.int32),
+                                       _dev(c.free_count, "free_count", torch.int32),
+                                       _dev(c.kv_status, "kv_status", torch.int32), _stream_ptr(stream, dev)))
+
+
+def attn_paged_prefill(q, k_pool, v_pool, block_table, context_lens, token_start, scale=None, o=None, lse=None,
+                       stream=None, with_lse=True):
+    """O [N,Hq,D] (and LSE [N,Hq]) of the new tokens q [N,Hq,D] of a ragged batch over a
+    paged cache: row token_start[s] + j is token j of sequence s, at position
+    context_lens[s] - n_s + j, and attends to positions 0 .. that one (async)."""
+    dev = _same_device(q, k_pool, v_pool, block_table, context_lens, token_start)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("expected q [N,Hq,D] and pools [num_pages,Hkv,page_size,D]")
+    N, Hq, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_pool.shape
+    S = block_table.shape[0]
+    if Dk != D or block_table.dim() != 2 or context_lens.shape != (S,) or token_start.shape != (S + 1,):
+        raise ValueError("shape mismatch among q, pools, block_table, context_lens, token_start")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((N, Hq), device=dev, dtype=torch.float32)
+    lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    _check(lib().attn_paged_prefill(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                    _dev(block_table, "block_table", torch.int32),
+                                    _dev(context_lens, "context_lens", torch.int32),
+                                    _dev(token_start, "token_start", torch.int32), S, N, Hq, Hkv, D, page_size,
+                                    block_table.shape[1], num_pages, scale, _dev(o, "o"), lse_p,
+                                    _stream_ptr(stream, dev)))
+    return o, lse
 
 
 def attn_kv_release(seq_ids, cache, stream=None):

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_kv.hip", "attn_materialized.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_kv.hip", "attn_materialized.hip",
+           "attn_prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -382,6 +382,100 @@ attn_status attn_kv_append(const float* k_new, const float* v_new, int64_t S, in
     }
 }
 
+attn_status attn_kv_append_tokens(const float* k_new, const float* v_new, const int32_t* token_start, int64_t S,
+                                  int64_t N, int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages_per_seq,
+                                  int64_t num_pages, float* k_pool, float* v_pool, int32_t* block_table,
+                                  int32_t* context_lens, int32_t* free_pages, int32_t* free_count,
+                                  int32_t* kv_status, void* stream) {
+    try {
+        ATTN_TRY(check_kv_shape("attn_kv_append_tokens", S, page_size, max_pages_per_seq, num_pages));
+        if (Hkv <= 0 || D <= 0 || N < 0)
+            return fail(ATTN_INVALID_ARGUMENT, "attn_kv_append_tokens: Hkv and D must be positive and N >= 0");
+        if (num_pages * Hkv * page_size * D >= ((int64_t)1 << 40) || N * Hkv * D >= kMaxElems || S + 1 >= kMaxElems)
+            return fail(ATTN_INVALID_ARGUMENT, "attn_kv_append_tokens: pool or rows too large");
+        if (!attn::causal_head_dim_supported(D))
+            return fail(ATTN_UNSUPPORTED, "attn_kv_append_tokens: head width D=" + std::to_string(D) +
+                                              " is not one of 8, 16, 32, 64, 128");
+        if (N > 0) {
+            ATTN_TRY(check_ptr(k_new, "k_new", 16));
+            ATTN_TRY(check_ptr(v_new, "v_new", 16));
+        }
+        ATTN_TRY(check_ptr(token_start, "token_start", 4));
+        ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
+        ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
+        ATTN_TRY(check_ptr(block_table, "block_table", 4));
+        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+        ATTN_TRY(check_ptr(free_pages, "free_pages", 4));
+        ATTN_TRY(check_ptr(free_count, "free_count", 4));
+        ATTN_TRY(check_ptr(kv_status, "kv_status", 4));
+        const size_t nb = (size_t)(N * Hkv * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
+        const Range kn{k_new, N > 0 ? nb : 0, "k_new"}, vn{v_new, N > 0 ? nb : 0, "v_new"};
+        ATTN_TRY(check_disjoint({{k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
+                                 {block_table, (size_t)(S * max_pages_per_seq) * 4, "block_table"},
+                                 {context_lens, (size_t)S * 4, "context_lens"},
+                                 {free_pages, (size_t)num_pages * 4, "free_pages"}, {free_count, 4, "free_count"},
+                                 {kv_status, 4, "kv_status"}},
+                                {kn, vn, {token_start, (size_t)(S + 1) * 4, "token_start"}}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::KvAppendTokensArgs a{k_new, v_new, token_start, k_pool, v_pool, block_table, context_lens,
+                                   free_pages, free_count, kv_status, S, N, Hkv, D, page_size,
+                                   max_pages_per_seq, num_pages};
+        return launched(attn::launch_kv_append_tokens(a, (hipStream_t)stream), "attn_kv_append_tokens launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_kv_append_tokens: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_kv_append_tokens: unknown exception");
+    }
+}
+
+attn_status attn_paged_prefill(const float* q, const float* k_pool, const float* v_pool, const int32_t* block_table,
+                               const int32_t* context_lens, const int32_t* token_start, int64_t S, int64_t N,
+                               int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages_per_seq,
+                               int64_t num_pages, float scale, float* o, float* lse, void* stream) {
+    try {
+        if (S <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 ||
+            num_pages <= 0)
+            return fail(ATTN_INVALID_ARGUMENT, "attn_paged_prefill: S, N, Hq, Hkv, D, page_size, "
+                                               "max_pages_per_seq and num_pages must all be positive");
+        if (Hq % Hkv != 0)
+            return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads");
+        if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
+        if (page_size * max_pages_per_seq >= kMaxElems || S * max_pages_per_seq >= kMaxElems ||
+            N * Hq * D >= kMaxElems || (N / 64 + S) * Hq >= kMaxElems ||
+            num_pages * Hkv * page_size * D >= ((int64_t)1 << 40))
+            return fail(ATTN_INVALID_ARGUMENT, "attn_paged_prefill: sizes too large");
+        if (!attn::causal_head_dim_supported(D) || (page_size != 16 && page_size != 32 && page_size != 64))
+            return fail(ATTN_UNSUPPORTED, "attn_paged_prefill: no kernel for D=" + std::to_string(D) +
+                                              ", page_size=" + std::to_string(page_size) +
+                                              " (supported: D in {8,16,32,64,128}, page_size in {16,32,64})");
+        ATTN_TRY(check_ptr(q, "q", 16));
+        ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
+        ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
+        ATTN_TRY(check_ptr(block_table, "block_table", 4));
+        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+        ATTN_TRY(check_ptr(token_start, "token_start", 4));
+        ATTN_TRY(check_ptr(o, "o", 16));
+        if (lse) ATTN_TRY(check_ptr(lse, "lse", 4));
+        const size_t qb = (size_t)(N * Hq * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
+        const Range lr{lse, lse ? (size_t)(N * Hq) * 4 : 0, "lse"};
+        ATTN_TRY(check_disjoint({{o, qb, "o"}, lr},
+                                {{q, qb, "q"}, {k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
+                                 {block_table, (size_t)(S * max_pages_per_seq) * 4, "block_table"},
+                                 {context_lens, (size_t)S * 4, "context_lens"},
+                                 {token_start, (size_t)(S + 1) * 4, "token_start"}}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        attn::PrefillArgs a{q, k_pool, v_pool, block_table, context_lens, token_start, o, lse,
+                            S, N, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale};
+        return launched(attn::launch_paged_prefill(a, (hipStream_t)stream), "attn_paged_prefill launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_prefill: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_paged_prefill: unknown exception");
+    }
+}
+
 attn_status attn_kv_release(const int32_t* seq_ids, int64_t n, int64_t S, int64_t page_size,
                             int64_t max_pages_per_seq, int64_t num_pages, int32_t* block_table,
                             int32_t* context_lens, int32_t* free_pages, int32_t* free_count, int32_t* kv_status,

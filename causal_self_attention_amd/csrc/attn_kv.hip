@@ -19,6 +19,9 @@
 //      vectors) and advances the sequence's length.
 //   attn_kv_release (one work-group) pushes the pages of the given sequences
 //   back, in order, and zeroes their lengths.
+//   attn_kv_append_tokens does the same for a ragged batch of several new rows per
+//   sequence (the step before a batched prefill): one lease work-group, then one
+//   wave per new row.
 // The work is a few kilobytes per call; the kernels are latency bound by design
 // (one block-wide scan, one vector copy), not HBM bound.
 #include "attn_launch.h"
@@ -151,6 +154,108 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_release_kernel(
         *FCOUNT = top + total;
         *STATUS = ATTN_KV_OK;
     }
+}
+
+// Ragged multi-token append (the step before a batched prefill): sequence s brings
+// n_s = token_start[s+1] - token_start[s] new rows.  One work-group leases, in index
+// order, the pages each sequence's new positions start -- sequence s's k-th new page
+// (logical order) is the (o_s + k)-th from the top of the stack, o_s the pages taken
+// by the sequences before it -- records them in the table and sets the new lengths;
+// if a sequence would pass its capacity or the stack is short it writes the status
+// and changes nothing.  (With one token per sequence this is the single-token lease.)
+__device__ __forceinline__ int tokens_of(const int32_t* __restrict__ TS, int s, int N) {
+    const int a = min(max(TS[s], 0), N), b = min(max(TS[s + 1], 0), N);
+    return max(b - a, 0);  // a broken (decreasing) table counts as no tokens
+}
+
+__global__ __launch_bounds__(kScanThreads) void attn_kv_lease_tokens_kernel(
+    int32_t* __restrict__ BT, int32_t* __restrict__ CTX, const int32_t* __restrict__ TS,
+    const int32_t* __restrict__ FREE, int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int N,
+    int PS, int max_pages) {
+    __shared__ int buf[kScanThreads];
+    const int tid = threadIdx.x;
+    const int cap = PS * max_pages;
+    auto new_pages = [&](int t, int n) { return (t + n + PS - 1) / PS - (t + PS - 1) / PS; };
+    int needed = 0, full = 0;
+    for (int base = 0; base < S; base += kScanThreads) {
+        const int s = base + tid;
+        const int t = s < S ? max(CTX[s], 0) : 0;
+        const int n = s < S ? tokens_of(TS, s, N) : 0;
+        int tot;
+        block_exclusive_scan(s < S && t + n > cap ? 1 : 0, buf, &tot);
+        full += tot;
+        block_exclusive_scan(s < S && t + n <= cap ? new_pages(t, n) : 0, buf, &tot);
+        needed += tot;
+    }
+    const int top = *FCOUNT;
+    if (full > 0 || needed > top) {
+        if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
+        return;  // uniform
+    }
+    int offset = 0;
+    for (int base = 0; base < S; base += kScanThreads) {
+        const int s = base + tid;
+        const int t = s < S ? max(CTX[s], 0) : 0;
+        const int n = s < S ? tokens_of(TS, s, N) : 0;
+        const int np = s < S ? new_pages(t, n) : 0;
+        int tot;
+        const int rank = offset + block_exclusive_scan(np, buf, &tot);
+        const int p0 = (t + PS - 1) / PS;  // first logical page to lease
+        for (int k = 0; k < np; ++k) BT[(size_t)s * max_pages + p0 + k] = FREE[top - 1 - (rank + k)];
+        if (s < S) CTX[s] = t + n;
+        offset += tot;
+    }
+    if (tid == 0) {
+        *FCOUNT = top - needed;
+        *STATUS = ATTN_KV_OK;
+    }
+}
+
+// One wave per new row r: its sequence is the last s with token_start[s] <= r (a
+// ballot over the table, 64 sequences at a time), its position new_length - n_s +
+// (r - token_start[s]); the Hkv x D key and value rows go to that page slot.
+__global__ __launch_bounds__(256) void attn_kv_write_tokens_kernel(
+    const float* __restrict__ Kn, const float* __restrict__ Vn, float* __restrict__ Kp, float* __restrict__ Vp,
+    const int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, const int32_t* __restrict__ TS,
+    const int32_t* __restrict__ STATUS, int S, int N, int Hkv, int D, int PS, int max_pages, int num_pages) {
+    if (*STATUS != ATTN_KV_OK) return;  // uniform: the lease failed, change nothing
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (r >= N) return;  // wave-uniform
+    int count = 0;  // sequences s < S with token_start[s] <= r
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        const int s = c0 + lane;
+        count += __popcll(__ballot(s < S && TS[min(s, S - 1)] <= r));
+    }
+    const int s = count - 1;
+    if (s < 0) return;  // wave-uniform: r precedes every sequence (a broken table)
+    const int n = tokens_of(TS, s, N);
+    const int j = r - TS[s];
+    if (j < 0 || j >= n) return;  // wave-uniform: not a row of sequence s
+    const int pos = CTX[s] - n + j;
+    if (pos < 0 || pos >= PS * max_pages) return;  // wave-uniform; a broken state
+    const int page = min(max(BT[(size_t)s * max_pages + pos / PS], 0), num_pages - 1);
+    const int d4 = D / 4;
+    for (int idx = lane; idx < Hkv * d4; idx += 64) {
+        const int h = idx / d4, c = idx % d4;
+        const size_t src = ((size_t)r * Hkv + h) * D + 4 * c;
+        const size_t dst = (((size_t)page * Hkv + h) * PS + pos % PS) * D + 4 * c;
+        *(f32x4*)(Kp + dst) = *(const f32x4*)(Kn + src);
+        *(f32x4*)(Vp + dst) = *(const f32x4*)(Vn + src);
+    }
+}
+
+hipError_t launch_kv_append_tokens(const KvAppendTokensArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_kv_lease_tokens_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.block_table,
+                       a.context_lens, a.token_start, a.free_pages, a.free_count, a.status, (int)a.S, (int)a.N,
+                       (int)a.page_size, (int)a.max_pages);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.N == 0) return e;
+    hipLaunchKernelGGL(attn_kv_write_tokens_kernel, dim3((unsigned)((a.N + 3) / 4)), dim3(256), 0, stream, a.k_new,
+                       a.v_new, a.k_pool, a.v_pool, a.block_table, a.context_lens, a.token_start, a.status,
+                       (int)a.S, (int)a.N, (int)a.Hkv, (int)a.D, (int)a.page_size, (int)a.max_pages,
+                       (int)a.num_pages);
+    return hipGetLastError();
 }
 
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {

@@ -54,6 +54,22 @@ struct KvAppendArgs {
     int64_t S, Hkv, D, page_size, max_pages, num_pages;
 };
 
+struct KvAppendTokensArgs {
+    const float *k_new, *v_new;  // [N, Hkv, D]
+    const int32_t* token_start;  // [S + 1]
+    float *k_pool, *v_pool;
+    int32_t *block_table, *context_lens, *free_pages, *free_count, *status;
+    int64_t S, N, Hkv, D, page_size, max_pages, num_pages;
+};
+
+struct PrefillArgs {
+    const float *q, *k_pool, *v_pool;  // q [N, Hq, D]
+    const int32_t *block_table, *context_lens, *token_start;
+    float *o, *lse;  // o [N, Hq, D]; lse [N, Hq] or NULL
+    int64_t S, N, Hq, Hkv, D, page_size, max_pages, num_pages;
+    float scale;
+};
+
 struct KvReleaseArgs {
     const int32_t* seq_ids;
     int64_t n, S;
@@ -89,6 +105,8 @@ hipError_t launch_mat_delta(const float* p, const float* dpx, float* delta, int6
                             hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+hipError_t launch_kv_append_tokens(const KvAppendTokensArgs& a, hipStream_t stream);
+hipError_t launch_paged_prefill(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_kv_release(const KvReleaseArgs& a, hipStream_t stream);
 
 }  // namespace attn

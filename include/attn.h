@@ -21,12 +21,18 @@
  *                      limits"; "What the Metal slice does": the materialized
  *                      path returns probabilities and context and keeps P for
  *                      the VJPs; the probability diagnostic always takes it).
+ *   attn_paged_prefill  batched prefill: the new tokens of a ragged batch of
+ *                      sequences attend causally to their sequence's paged K/V
+ *                      (same sections; the pages prefill one token at a time
+ *                      through the decode op, this takes all of them at once).
  *   attn_kv_append     the step before decode: lease pages from a device-resident
  *   attn_kv_release    free list and append each sequence's newest K/V rows, or
  *                      return a finished sequence's pages ("Architecture",
  *                      "Serving boundary": a request's logical page table, pages
  *                      leased from shared per-layer pools; "Incremental
  *                      attention": [physical_page, H, page_offset, d_h] pools).
+ *   attn_kv_append_tokens  the same append for a ragged batch of several new
+ *                      rows per sequence (the step before attn_paged_prefill).
  *
  * Conventions ("Architecture", "Tensor conventions"): contiguous row-major
  * float32; scores are [B,H,Tq,Tk] with Tq = Tk = T; the key at position t_k is
@@ -59,7 +65,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 0x00010002u /* 1.2: major << 16 | minor */
+#define ATTN_ABI_VERSION 0x00010003u /* 1.3: major << 16 | minor */
 
 typedef int32_t attn_status;
 enum {
@@ -158,6 +164,36 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Batched prefill over a paged K/V cache, for a ragged batch: sequence s brings
+ * n_s = token_start[s+1] - token_start[s] new tokens (n_s may be 0), whose K/V
+ * rows are already in the cache (attn_kv_append_tokens), so that it now holds
+ * context_lens[s] >= n_s positions.  New token j of sequence s sits at position
+ *   t = context_lens[s] - n_s + j
+ * and attends to positions 0 .. t of its sequence (keys past t are excluded), each
+ * read in place through the block table as in attn_paged_decode.
+ *   q             [N, Hq, D]      new tokens' queries, sequence by sequence:
+ *                                 row token_start[s] + j is token j of sequence s
+ *   k_pool, v_pool [num_pages, Hkv, page_size, D]
+ *   block_table   [S, max_pages_per_seq] int32;  context_lens [S] int32
+ *   token_start   [S + 1] int32   nondecreasing, token_start[0] = 0, token_start[S] = N
+ *   o             [N, Hq, D]      out;  lse [N, Hq] or NULL: out, natural log
+ * N >= 1.  q, pools, o 16-byte aligned; int32 arrays and lse 4-byte aligned; o and
+ * lse overlap no input or each other.  D in {8,16,32,64,128}, page_size in
+ * {16,32,64}, Hq % Hkv == 0.  With n_s = 1 for every s this is attn_paged_decode;
+ * with context_lens[s] = n_s it is attn_causal_fwd on the sequence's rows.
+ * Device-side preconditions (not checked on the host; violated ones give wrong
+ * numbers but never an out-of-bounds access): the token_start properties above,
+ * n_s <= context_lens[s] <= max_pages_per_seq * page_size, and table entries
+ * below ceil(context_lens[s] / page_size) in [0, num_pages).
+ */
+attn_status attn_paged_prefill(const float* q, const float* k_pool, const float* v_pool,
+                               const int32_t* block_table, const int32_t* context_lens,
+                               const int32_t* token_start, int64_t S, int64_t N,
+                               int64_t Hq, int64_t Hkv, int64_t D,
+                               int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
+                               float scale, float* o, float* lse, void* stream);
+
+/*
  * Materialized causal attention: the same O and LSE as attn_causal_fwd, plus
  *   p  [B, Hq, T, T] float32   p[b,h,i,j] = exp(scale q_i.k_j - lse[b,h,i]) for
  *                              j <= i and 0 for j > i (every row sums to 1).
@@ -235,6 +271,30 @@ attn_status attn_kv_append(const float* k_new, const float* v_new,
                            int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
                            float* k_pool, float* v_pool, int32_t* block_table, int32_t* context_lens,
                            int32_t* free_pages, int32_t* free_count, int32_t* kv_status, void* stream);
+
+/*
+ * Appends n_s = token_start[s+1] - token_start[s] positions (n_s >= 0) to each of
+ * the S sequences:
+ *   k_new, v_new  [N, Hkv, D] float32   new rows, sequence by sequence: row
+ *                                       token_start[s] + j is sequence s's j-th
+ *   token_start   [S + 1] int32         nondecreasing, 0 .. N
+ * For sequence s with t = context_lens[s]: the logical pages t / page_size ..
+ * (t + n_s - 1) / page_size that do not exist yet are leased -- over all sequences
+ * in index order, and within a sequence in logical order, the r-th page leased is
+ * free_pages[free_count - 1 - r]; free_count drops by their number -- then
+ *   pool[block_table[s, (t + j) / page_size], h, (t + j) % page_size, :] = new row j
+ * for every KV head h, and context_lens[s] = t + n_s.  With n_s = 1 for every s
+ * this is attn_kv_append.  kv_status as there: ATTN_KV_SEQUENCE_FULL if some
+ * t + n_s exceeds max_pages_per_seq * page_size, ATTN_KV_POOL_EXHAUSTED if fewer
+ * pages are free than leased; then nothing changes.  N >= 0 (k_new and v_new may
+ * be NULL when N == 0).  Alignment and overlap rules as for attn_kv_append;
+ * token_start is an input.
+ */
+attn_status attn_kv_append_tokens(const float* k_new, const float* v_new, const int32_t* token_start,
+                                  int64_t S, int64_t N, int64_t Hkv, int64_t D,
+                                  int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
+                                  float* k_pool, float* v_pool, int32_t* block_table, int32_t* context_lens,
+                                  int32_t* free_pages, int32_t* free_count, int32_t* kv_status, void* stream);
 
 /*
  * Returns the pages of sequences seq_ids[0 .. n-1] (distinct indices in [0, S))

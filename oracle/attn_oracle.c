@@ -207,6 +207,25 @@ int oracle_decode_dense(const double* q, const double* kseq, const double* vseq,
     return 0;
 }
 
+/* Sequence s's first n positions, resolved position by position through its page
+ * table into contiguous kseq, vseq [n,Hkv,D]: position t of the sequence lives at
+ *   pool[block_table[s, t / page_size], g, t % page_size, :].
+ * Returns -1 on a page index outside the pool.  */
+static int gather_paged(const double* k_pool, const double* v_pool, const int32_t* block_table, int64_t s,
+                        int64_t n, int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages,
+                        int64_t num_pages, double* kseq, double* vseq) {
+    for (int64_t t = 0; t < n; ++t) {
+        const int64_t phys = block_table[s * max_pages + t / page_size];
+        if (phys < 0 || phys >= num_pages) return -1;
+        for (int64_t g = 0; g < Hkv; ++g) {
+            const int64_t src = ((phys * Hkv + g) * page_size + t % page_size) * D;
+            memcpy(kseq + (t * Hkv + g) * D, k_pool + src, (size_t)D * sizeof(double));
+            memcpy(vseq + (t * Hkv + g) * D, v_pool + src, (size_t)D * sizeof(double));
+        }
+    }
+    return 0;
+}
+
 /* Paged single-token decode over S independent sequences sharing one pool.
  * q, o: [S,Hq,D]; k_pool, v_pool: [num_pages,Hkv,page_size,D];
  * block_table: [S,max_pages] (logical page -> physical page); ctx: [S];
@@ -228,19 +247,55 @@ int oracle_paged_decode(const double* q, const double* k_pool, const double* v_p
         double* kseq = (double*)malloc((size_t)(n * Hkv * D) * sizeof(double));
         double* vseq = (double*)malloc((size_t)(n * Hkv * D) * sizeof(double));
         if (!kseq || !vseq) { free(kseq); free(vseq); failed = 1; continue; }
-        int bad = 0;
-        for (int64_t t = 0; t < n && !bad; ++t) {
-            const int64_t phys = block_table[s * max_pages + t / page_size];
-            if (phys < 0 || phys >= num_pages) { bad = 1; break; }
-            for (int64_t g = 0; g < Hkv; ++g) {
-                const int64_t src = ((phys * Hkv + g) * page_size + t % page_size) * D;
-                memcpy(kseq + (t * Hkv + g) * D, k_pool + src, (size_t)D * sizeof(double));
-                memcpy(vseq + (t * Hkv + g) * D, v_pool + src, (size_t)D * sizeof(double));
-            }
-        }
+        const int bad = gather_paged(k_pool, v_pool, block_table, s, n, Hkv, D, page_size, max_pages, num_pages,
+                                     kseq, vseq);
         if (bad || oracle_decode_dense(q + s * Hq * D, kseq, vseq, n, Hq, Hkv, D, scale,
                                        o + s * Hq * D, lse ? lse + s * Hq : NULL) != 0)
             failed = 1;
+        free(kseq);
+        free(vseq);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Batched prefill over S sequences sharing one pool ("Architecture", "Serving
+ * boundary"; "Execution Backends and the Python ABI", "Incremental attention":
+ * K/V read through the sequence's page table; "Tensor conventions": a key after
+ * the query is excluded).  Sequence s has n_s = token_start[s+1] - token_start[s]
+ * new tokens, whose queries are rows token_start[s] + j of q [N,Hq,D]; its cache
+ * holds ctx[s] >= n_s positions, so token j sits at position t = ctx[s] - n_s + j.
+ * Each row is the plain definition: softmax over the scores of positions 0..t,
+ * then the weighted sum of their values -- i.e. the dense decode definition over
+ * the first t + 1 gathered positions.  o: [N,Hq,D]; lse: [N,Hq] or NULL.
+ * Returns -1 on a bad table, length or page index.  */
+int oracle_paged_prefill(const double* q, const double* k_pool, const double* v_pool,
+                         const int32_t* block_table, const int32_t* ctx, const int32_t* token_start,
+                         int64_t S, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
+                         int64_t max_pages, int64_t num_pages, double scale, double* o, double* lse) {
+    if (S <= 0 || N < 0 || page_size <= 0 || max_pages <= 0 || token_start[0] != 0 || token_start[S] != N)
+        return -1;
+    for (int64_t s = 0; s < S; ++s)
+        if (token_start[s + 1] < token_start[s]) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t s = 0; s < S; ++s) {
+        const int64_t n_new = token_start[s + 1] - token_start[s];
+        const int64_t n = ctx[s];
+        if (n_new == 0) continue;
+        if (n < n_new || n > max_pages * page_size) { failed = 1; continue; }
+        double* kseq = (double*)malloc((size_t)(n * Hkv * D) * sizeof(double));
+        double* vseq = (double*)malloc((size_t)(n * Hkv * D) * sizeof(double));
+        if (!kseq || !vseq) { free(kseq); free(vseq); failed = 1; continue; }
+        int bad = gather_paged(k_pool, v_pool, block_table, s, n, Hkv, D, page_size, max_pages, num_pages, kseq,
+                               vseq);
+        for (int64_t j = 0; j < n_new && !bad; ++j) {
+            const int64_t row = token_start[s] + j;
+            const int64_t pos = n - n_new + j;
+            if (oracle_decode_dense(q + row * Hq * D, kseq, vseq, pos + 1, Hq, Hkv, D, scale, o + row * Hq * D,
+                                    lse ? lse + row * Hq : NULL) != 0)
+                bad = 1;
+        }
+        if (bad) failed = 1;
         free(kseq);
         free(vseq);
     }

@@ -63,6 +63,39 @@ class KvCacheModel:
         self.status = KV_OK
         return self.status
 
+    def append_tokens(self, k_new, v_new, token_start):
+        """Append rows token_start[s] .. token_start[s+1]-1 of k_new, v_new ([N, Hkv, D])
+        to sequence s, for every s.  The pages the new positions start are leased from
+        the top of the stack: sequences in index order, each one's pages in logical
+        order."""
+        capacity = self.page_size * self.max_pages
+        lengths = [int(t) for t in self.context_lens]
+        counts = [int(token_start[s + 1]) - int(token_start[s]) for s in range(self.S)]
+        if any(lengths[s] + counts[s] > capacity for s in range(self.S)):
+            self.status = KV_SEQUENCE_FULL
+            return self.status
+        # logical pages that do not exist yet: ceil(t / page) .. ceil((t + n) / page) - 1
+        new_pages = []
+        for s in range(self.S):
+            first = -(-lengths[s] // self.page_size)
+            last = -(-(lengths[s] + counts[s]) // self.page_size)
+            new_pages.extend((s, p) for p in range(first, last))
+        if len(new_pages) > self.free_count:
+            self.status = KV_POOL_EXHAUSTED
+            return self.status
+        for r, (s, p) in enumerate(new_pages):
+            self.block_table[s, p] = int(self.free_pages[self.free_count - 1 - r])
+        self.free_count -= len(new_pages)
+        for s in range(self.S):
+            for j in range(counts[s]):
+                t = lengths[s] + j
+                page = int(self.block_table[s, t // self.page_size])
+                self.k_pool[page, :, t % self.page_size, :] = k_new[int(token_start[s]) + j]
+                self.v_pool[page, :, t % self.page_size, :] = v_new[int(token_start[s]) + j]
+            self.context_lens[s] = lengths[s] + counts[s]
+        self.status = KV_OK
+        return self.status
+
     def release(self, seq_ids):
         """Push the pages of seq_ids back (in list order, each sequence's pages in
         logical order) and zero their lengths."""

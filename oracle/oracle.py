@@ -52,8 +52,10 @@ class Oracle:
                                             ctypes.c_double, _dp, _dp]
         lib.oracle_paged_decode.argtypes = [_dp, _dp, _dp, _ip, _ip, _i64, _i64, _i64, _i64,
                                             _i64, _i64, _i64, ctypes.c_double, _dp, _dp]
+        lib.oracle_paged_prefill.argtypes = [_dp, _dp, _dp, _ip, _ip, _ip, _i64, _i64, _i64, _i64, _i64,
+                                             _i64, _i64, _i64, ctypes.c_double, _dp, _dp]
         for fn in ("oracle_causal_fwd", "oracle_causal_bwd", "oracle_decode_dense",
-                   "oracle_paged_decode", "oracle_num_threads"):
+                   "oracle_paged_decode", "oracle_paged_prefill", "oracle_num_threads"):
             getattr(lib, fn).restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
@@ -136,6 +138,26 @@ class Oracle:
         return o, lse
 
 
+    def paged_prefill(self, q, k_pool, v_pool, block_table, context_lens, token_start, scale=None):
+        """q [N,Hq,D]; pools [P,Hkv,page,D]; block_table [S,maxp]; ctx [S]; token_start [S+1]."""
+        q, k_pool, v_pool = _f64(q), _f64(k_pool), _f64(v_pool)
+        bt, ctx, ts = _i32(block_table), _i32(context_lens), _i32(token_start)
+        N, Hq, D = q.shape
+        P, Hkv, page, Dk = k_pool.shape
+        S = bt.shape[0]
+        if Dk != D or v_pool.shape != k_pool.shape or ctx.shape != (S,) or ts.shape != (S + 1,):
+            raise ValueError("incompatible shapes")
+        scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        o = np.zeros((N, Hq, D))
+        lse = np.zeros((N, Hq))
+        rc = self.lib.oracle_paged_prefill(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(bt, _ip), _ptr(ctx, _ip),
+                                           _ptr(ts, _ip), S, N, Hq, Hkv, D, page, bt.shape[1], P, scale,
+                                           _ptr(o), _ptr(lse))
+        if rc != 0:
+            raise RuntimeError("oracle_paged_prefill failed (bad table, length or page index?)")
+        return o, lse
+
+
 _default = None
 
 
@@ -160,3 +182,7 @@ def decode_dense(*a, **kw):
 
 def paged_decode(*a, **kw):
     return default().paged_decode(*a, **kw)
+
+
+def paged_prefill(*a, **kw):
+    return default().paged_prefill(*a, **kw)

@@ -31,6 +31,15 @@ DECODE_WORKLOADS = {
 }
 
 
+# Batched prefill into a paged cache (ragged): sequences with a cached prefix of
+# U{cached_lo..cached_hi} positions each bring U{new_lo..new_hi} new tokens.
+PREFILL_WORKLOADS = {
+    "paged_prefill_s8_hq16_hkv4_d64_p16": dict(S=8, Hq=16, Hkv=4, D=64, page_size=16, cached_lo=0,
+                                               cached_hi=2048, new_lo=128, new_hi=1024, max_pages=192,
+                                               seed=6),
+}
+
+
 def causal_inputs(B, Hq, Hkv, T, D, seed, do_std=1.0, with_do=True):
     """Q [B,Hq,T,D], K, V [B,Hkv,T,D] and (optionally) dO [B,Hq,T,D], fp32, CPU.
 
@@ -94,6 +103,50 @@ def decode_workload(name):
     c = DECODE_WORKLOADS[name]
     return paged_decode_inputs(c["S"], c["Hq"], c["Hkv"], c["D"], c["page_size"], c["ctx_lo"],
                                c["ctx_hi"], c["max_pages"], c["seed"])
+
+
+def paged_prefill_inputs(S, Hq, Hkv, D, page_size, cached_lo, cached_hi, new_lo, new_hi, max_pages, seed,
+                         pool_shuffle=True):
+    """A ragged prefill batch over a paged cache whose new tokens are already appended.
+
+    Draw order: cached lengths c_s (uniform integers in [cached_lo, cached_hi]), new
+    token counts n_s (uniform in [new_lo, new_hi]), the page permutation, Q [N,Hq,D]
+    (N = sum n_s, sequence by sequence), K pool, V pool [num_pages,Hkv,page_size,D].
+    context_lens = c_s + n_s; token_start [S+1] = 0, n_0, n_0 + n_1, ...  Pages are
+    laid out as in paged_decode_inputs (shuffled, one extra padding page).
+    """
+    if cached_hi + new_hi > max_pages * page_size:
+        raise ValueError("cached_hi + new_hi exceeds the block table's capacity")
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    cached = torch.randint(cached_lo, cached_hi + 1, (S,), generator=g, dtype=torch.int64)
+    new = torch.randint(new_lo, new_hi + 1, (S,), generator=g, dtype=torch.int64)
+    ctx = cached + new
+    n_pages = [int(math.ceil(int(c) / page_size)) for c in ctx]
+    total = sum(n_pages)
+    perm = torch.randperm(total, generator=g) if pool_shuffle else torch.arange(total)
+    block_table = torch.full((S, max_pages), total, dtype=torch.int32)
+    off = 0
+    for s, n in enumerate(n_pages):
+        block_table[s, :n] = perm[off:off + n].to(torch.int32)
+        off += n
+    N = int(new.sum())
+    token_start = torch.zeros((S + 1,), dtype=torch.int32)
+    token_start[1:] = torch.cumsum(new, 0).to(torch.int32)
+    q = torch.randn((N, Hq, D), generator=g, dtype=torch.float32)
+    k_pool = torch.randn((total + 1, Hkv, page_size, D), generator=g, dtype=torch.float32)
+    v_pool = torch.randn((total + 1, Hkv, page_size, D), generator=g, dtype=torch.float32)
+    return {
+        "q": q, "k_pool": k_pool, "v_pool": v_pool, "block_table": block_table,
+        "context_lens": ctx.to(torch.int32), "token_start": token_start, "page_size": page_size,
+        "num_pages": total + 1, "poison_page": total, "N": N,
+    }
+
+
+def prefill_workload(name):
+    """Inputs of one named prefill workload (see PREFILL_WORKLOADS)."""
+    c = PREFILL_WORKLOADS[name]
+    return paged_prefill_inputs(c["S"], c["Hq"], c["Hkv"], c["D"], c["page_size"], c["cached_lo"],
+                                c["cached_hi"], c["new_lo"], c["new_hi"], c["max_pages"], c["seed"])
 
 
 def gather_sequence(k_pool, v_pool, block_table, ctx, s, page_size):

@@ -16,7 +16,10 @@ mathematics fix:
   future keys, sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, LSE bounds;
 * GQA: grouped attention equals multi-head attention on repeat-interleaved K/V;
 * decode: dense decode equals the last row of the causal forward, and paged
-  decode equals dense decode on the gathered sequence for any page shuffle.
+  decode equals dense decode on the gathered sequence for any page shuffle;
+* prefill: each new token's row equals the causal forward's row at its position
+  over the gathered sequence, brute force agrees on tiny ragged batches, and one
+  new token per sequence is decode.
 
 The mutation test (test_oracle_mutants.py) builds broken copies of the oracle
 and checks that each one trips at least one of these pins.
@@ -24,6 +27,7 @@ and checks that each one trips at least one of these pins.
 import math
 
 import numpy as np
+import torch
 
 import synthetic_inputs as si
 
@@ -402,6 +406,91 @@ def pin_paged_equals_dense(orc):
     assert np.array_equal(o3, o2) and np.array_equal(lse3, lse2), "poisoned tail/padding"
 
 
+# ----------------------------------------------------------------------------
+# batched prefill over a paged cache
+# ----------------------------------------------------------------------------
+def _prefill_case(S, Hq, Hkv, D, ps, cached, new, seed):
+    """A ragged batch whose new tokens are the last rows of a full per-sequence Q."""
+    ctx = [c + n for c, n in zip(cached, new)]
+    maxp = max(1, max(-(-c // ps) for c in ctx))
+    rng = np.random.default_rng(seed)
+    n_pages = [-(-c // ps) for c in ctx]
+    total = sum(n_pages)
+    perm = rng.permutation(total)
+    bt = np.full((S, maxp + 1), total, dtype=np.int32)
+    off = 0
+    for s in range(S):
+        bt[s, :n_pages[s]] = perm[off:off + n_pages[s]]
+        off += n_pages[s]
+    kp = rng.standard_normal((total + 1, Hkv, ps, D))
+    vp = rng.standard_normal((total + 1, Hkv, ps, D))
+    qfull = [rng.standard_normal((c, Hq, D)) for c in ctx]
+    q = np.concatenate([qf[c - n:] for qf, c, n in zip(qfull, ctx, new)], 0) if sum(new) else np.zeros((0, Hq, D))
+    ts = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    return q, kp, vp, bt, np.array(ctx, dtype=np.int32), ts, qfull
+
+
+def pin_prefill_rows_are_causal_rows(orc):
+    """Token j of sequence s (position t = ctx - n + j) gets the causal forward's
+    row t over the sequence gathered through its table, O and LSE."""
+    for (S, Hq, Hkv, D, ps, cached, new, seed) in (
+            (3, 4, 2, 8, 4, [0, 5, 9], [6, 3, 4], 71),
+            (4, 2, 2, 5, 8, [17, 0, 1, 30], [2, 9, 0, 1], 72),
+            (2, 6, 1, 4, 4, [3, 0], [1, 13], 73)):
+        q, kp, vp, bt, ctx, ts, qfull = _prefill_case(S, Hq, Hkv, D, ps, cached, new, seed)
+        o, lse = orc.paged_prefill(q, kp, vp, bt, ctx, ts, 0.4)
+        for s in range(S):
+            n = new[s]
+            if n == 0:
+                continue
+            kseq, vseq = si.gather_sequence(torch.from_numpy(kp), torch.from_numpy(vp), torch.from_numpy(bt),
+                                            torch.from_numpy(ctx), s, ps)
+            qc = np.transpose(qfull[s], (1, 0, 2))[None]
+            kc = np.transpose(kseq.numpy(), (1, 0, 2))[None]
+            vc = np.transpose(vseq.numpy(), (1, 0, 2))[None]
+            oc, lsec = orc.causal_fwd(qc, kc, vc, 0.4)
+            c = int(ctx[s])
+            rows = slice(int(ts[s]), int(ts[s + 1]))
+            assert _rel(o[rows], np.transpose(oc[0, :, c - n:], (1, 0, 2))) < RTOL_EXACT, ("prefill row", s)
+            assert _rel(lse[rows], lsec[0, :, c - n:].T) < RTOL_EXACT, ("prefill lse", s)
+
+
+def pin_prefill_bruteforce(orc):
+    """Scalar loops: every new token sums exp(scale q.k) over the positions up to its
+    own (no max subtraction), read through the table one position at a time."""
+    S, Hq, Hkv, D, ps = 3, 4, 2, 3, 4
+    cached, new = [2, 0, 6], [3, 5, 1]
+    q, kp, vp, bt, ctx, ts, _ = _prefill_case(S, Hq, Hkv, D, ps, cached, new, 74)
+    o, lse = orc.paged_prefill(q, kp, vp, bt, ctx, ts, 0.7)
+    G = Hq // Hkv
+    for s in range(S):
+        for j in range(new[s]):
+            row = int(ts[s]) + j
+            t = int(ctx[s]) - new[s] + j
+            for h in range(Hq):
+                g = h // G
+                w, vals = [], []
+                for pos in range(t + 1):
+                    page = int(bt[s, pos // ps])
+                    kr = kp[page, g, pos % ps]
+                    w.append(math.exp(0.7 * sum(q[row, h, c] * kr[c] for c in range(D))))
+                    vals.append(vp[page, g, pos % ps])
+                z = sum(w)
+                assert abs(lse[row, h] - math.log(z)) < 1e-12 * max(1.0, abs(math.log(z)))
+                for c in range(D):
+                    ref = sum(wi * vi[c] for wi, vi in zip(w, vals)) / z
+                    assert abs(o[row, h, c] - ref) < 1e-12, ("prefill brute", s, j, h, c)
+
+
+def pin_prefill_single_tokens_are_decode(orc):
+    """One new token per sequence: prefill and paged decode give the same rows."""
+    d = si.paged_decode_inputs(S=5, Hq=4, Hkv=2, D=8, page_size=4, ctx_lo=1, ctx_hi=23, max_pages=6, seed=75)
+    o, lse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"], 0.35)
+    ts = np.arange(6, dtype=np.int32)
+    op, lsep = orc.paged_prefill(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"], ts, 0.35)
+    assert np.array_equal(o, op) and np.array_equal(lse, lsep)
+
+
 ALL_PINS = [
     pin_bruteforce_forward,
     pin_bruteforce_backward,
@@ -416,4 +505,7 @@ ALL_PINS = [
     pin_gqa_identity,
     pin_decode_is_last_causal_row,
     pin_paged_equals_dense,
+    pin_prefill_rows_are_causal_rows,
+    pin_prefill_bruteforce,
+    pin_prefill_single_tokens_are_decode,
 ]

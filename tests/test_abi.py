@@ -54,7 +54,7 @@ def test_header_is_c11_clean(tmp_path):
 
 
 def test_version_and_status_values(L):
-    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010002
+    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010003
     header = open(HEADER).read()
     for name in ("ATTN_OK", "ATTN_INVALID_ARGUMENT", "ATTN_UNSUPPORTED", "ATTN_WORKSPACE_TOO_SMALL",
                  "ATTN_DEVICE_ERROR"):
@@ -123,6 +123,22 @@ def _matb(L, B=1, Hq=2, Hkv=2, T=16, D=8, scale=0.35, ws_bytes=None, **ptrs):
         ws_bytes = attn.attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
     return L.attn_materialized_bwd(p["q"], p["k"], p["v"], p["o"], p["p"], p["dout"], p["dp"], B, Hq, Hkv, T, D,
                                    scale, p["dq"], p["dk"], p["dv"], p["ws"], ws_bytes, None)
+
+
+def _pre(L, S=3, N=40, Hq=4, Hkv=2, D=64, page=16, maxp=8, npages=16, scale=0.125, **ptrs):
+    names = ["q", "kp", "vp", "bt", "ctx", "ts", "o", "lse"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_paged_prefill(p["q"], p["kp"], p["vp"], p["bt"], p["ctx"], p["ts"], S, N, Hq, Hkv, D, page, maxp,
+                                npages, scale, p["o"], p["lse"], None)
+
+
+def _appt(L, S=3, N=40, Hkv=2, D=64, page=16, maxp=4, npages=8, **ptrs):
+    names = ["kn", "vn", "ts", "kp", "vp", "bt", "ctx", "free", "fc", "st"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_kv_append_tokens(p["kn"], p["vn"], p["ts"], S, N, Hkv, D, page, maxp, npages, p["kp"], p["vp"],
+                                   p["bt"], p["ctx"], p["free"], p["fc"], p["st"], None)
 
 
 def _app(L, S=3, Hkv=2, D=64, page=16, maxp=4, npages=8, **ptrs):
@@ -204,6 +220,24 @@ def test_materialized_invalid_arguments(L):
     _expect(_matb(L, scale=float("nan")), attn.ATTN_INVALID_ARGUMENT, "scale")
 
 
+def test_prefill_invalid_arguments(L):
+    _expect(_pre(L, q=None), attn.ATTN_INVALID_ARGUMENT, "'q' is NULL")
+    _expect(_pre(L, ts=None), attn.ATTN_INVALID_ARGUMENT, "'token_start' is NULL")
+    _expect(_pre(L, N=0), attn.ATTN_INVALID_ARGUMENT, "positive")
+    _expect(_pre(L, Hq=3, Hkv=2), attn.ATTN_INVALID_ARGUMENT, "Hq % Hkv")
+    _expect(_pre(L, D=24), attn.ATTN_UNSUPPORTED, "D=24")
+    _expect(_pre(L, page=8), attn.ATTN_UNSUPPORTED, "page_size=8")
+    _expect(_pre(L, scale=float("inf")), attn.ATTN_INVALID_ARGUMENT, "scale")
+    _expect(_pre(L, o=_p(0)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'q'")
+    _expect(_pre(L, lse=_p(6)), attn.ATTN_INVALID_ARGUMENT, "overlap")  # lse == o
+    _expect(_pre(L, ts=ctypes.c_void_p(0x600000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
+    _expect(_appt(L, ts=None), attn.ATTN_INVALID_ARGUMENT, "'token_start' is NULL")
+    _expect(_appt(L, N=-1), attn.ATTN_INVALID_ARGUMENT, "N >= 0")
+    _expect(_appt(L, page=48), attn.ATTN_UNSUPPORTED, "page_size")
+    _expect(_appt(L, bt=_p(2)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'token_start'")
+    _expect(_appt(L, kn=None), attn.ATTN_INVALID_ARGUMENT, "'k_new' is NULL")
+
+
 def test_kv_invalid_arguments(L):
     _expect(_app(L, kn=None), attn.ATTN_INVALID_ARGUMENT, "'k_new' is NULL")
     _expect(_app(L, st=None), attn.ATTN_INVALID_ARGUMENT, "'kv_status' is NULL")
@@ -248,6 +282,10 @@ def test_valid_call_without_device_reports_device_error(L):
     _expect(_matb(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_matb(L, dp=None), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_app(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_appt(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_appt(L, N=0, kn=None, vn=None), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_pre(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_pre(L, lse=None), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_rel(L), attn.ATTN_DEVICE_ERROR, "device")
 
 

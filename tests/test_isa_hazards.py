@@ -36,7 +36,8 @@ def test_checker_flags_a_branch_into_the_read():
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_kv.hip", "attn_materialized.hip"])
+@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_kv.hip", "attn_materialized.hip",
+                                 "attn_prefill.hip"])
 def test_kernel_assembly_has_no_short_mfma_read_paths(src, tmp_path):
     out = tmp_path / (src + ".s")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",

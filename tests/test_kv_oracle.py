@@ -161,3 +161,86 @@ def test_release_overflow_is_refused_and_changes_nothing():
     before = _snapshot(m)
     assert m.release([0]) == KV_STACK_OVERFLOW
     assert _same(before, _snapshot(m))
+
+
+# ----------------------------------------------------------------------------
+# ragged multi-token append (the step before a batched prefill)
+# ----------------------------------------------------------------------------
+def test_append_tokens_gathered_stream_and_accounting():
+    """Ragged appends (some sequences adding nothing, some crossing several pages):
+    what is read back equals what was appended, and the page accounting holds."""
+    rng = np.random.default_rng(11)
+    S, Hkv, D, ps, max_pages, num_pages = 4, 2, 4, 16, 6, 20
+    m = KvCacheModel(S, Hkv, D, ps, max_pages, num_pages)
+    streams = [([], []) for _ in range(S)]
+    for step in range(60):
+        if step % 17 == 16:
+            ids = sorted(rng.choice(S, size=int(rng.integers(1, S)), replace=False).tolist())
+            assert m.release(ids) == KV_OK
+            for s in ids:
+                streams[s] = ([], [])
+            continue
+        counts = rng.integers(0, 40, size=S)
+        ts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        kn = rng.standard_normal((int(ts[-1]), Hkv, D)).astype(np.float32)
+        vn = rng.standard_normal((int(ts[-1]), Hkv, D)).astype(np.float32)
+        before = _snapshot(m)
+        st = m.append_tokens(kn, vn, ts)
+        if st == KV_OK:
+            for s in range(S):
+                streams[s][0].extend(kn[ts[s]:ts[s + 1]])
+                streams[s][1].extend(vn[ts[s]:ts[s + 1]])
+        else:
+            assert st in (KV_POOL_EXHAUSTED, KV_SEQUENCE_FULL)
+            assert _same(before, _snapshot(m)), "a refused append changed the state"
+        _check_accounting(m)
+        for s in range(S):
+            ks, vs = m.gather(s)
+            assert len(ks) == len(streams[s][0])
+            if len(ks):
+                assert np.array_equal(ks, np.stack(streams[s][0])) and np.array_equal(vs, np.stack(streams[s][1]))
+
+
+def test_append_tokens_one_each_is_append():
+    """One new row per sequence: the same state as the single-token append."""
+    rng = np.random.default_rng(12)
+    S, Hkv, D, ps = 3, 2, 4, 16
+    a = KvCacheModel(S, Hkv, D, ps, 3, 8)
+    b = KvCacheModel(S, Hkv, D, ps, 3, 8)
+    ts = np.arange(S + 1, dtype=np.int32)
+    for _ in range(40):
+        kn, vn = _rows(rng, S, Hkv, D), _rows(rng, S, Hkv, D)
+        assert a.append(kn, vn) == b.append_tokens(kn, vn, ts)
+        assert _same(_snapshot(a), _snapshot(b))
+
+
+def test_append_tokens_worked_example():
+    """Lengths [15, 0, 32], page 16, 8 pages, stack top = page 0.  Adding [3, 20, 0]
+    rows: sequence 0 needs logical page 1 (positions 16, 17), sequence 1 logical pages
+    0 and 1, sequence 2 nothing -> pages 0 | 1, 2 from the top, in that order."""
+    m = KvCacheModel(3, 1, 4, 16, 4, 8)
+    m.context_lens[:] = [15, 0, 32]
+    m.block_table[0, 0] = 7
+    m.block_table[2, :2] = [6, 5]
+    m.free_pages[:5] = [4, 3, 2, 1, 0]
+    m.free_count = 5
+    ts = np.array([0, 3, 23, 23], dtype=np.int32)
+    kn = np.arange(23 * 4, dtype=np.float32).reshape(23, 1, 4)
+    assert m.append_tokens(kn, -kn, ts) == KV_OK
+    assert m.block_table[0, :2].tolist() == [7, 0]
+    assert m.block_table[1, :2].tolist() == [1, 2]
+    assert m.block_table[2, :2].tolist() == [6, 5]
+    assert m.context_lens.tolist() == [18, 20, 32] and m.free_count == 2
+    assert np.array_equal(m.k_pool[7, 0, 15], kn[0, 0]) and np.array_equal(m.k_pool[0, 0, 1], kn[2, 0])
+    assert np.array_equal(m.k_pool[2, 0, 3], kn[3 + 19, 0]) and np.array_equal(m.v_pool[1, 0, 0], -kn[3, 0])
+
+
+def test_append_tokens_refusals_change_nothing():
+    m = KvCacheModel(2, 1, 4, 16, 2, 3)
+    ts = np.array([0, 33, 33], dtype=np.int32)  # 33 > 2 pages of 16
+    before = _snapshot(m)
+    assert m.append_tokens(np.zeros((33, 1, 4), np.float32), np.zeros((33, 1, 4), np.float32), ts) == KV_SEQUENCE_FULL
+    assert _same(before, _snapshot(m))
+    ts = np.array([0, 32, 64], dtype=np.int32)  # 4 pages needed, 3 free
+    assert m.append_tokens(np.zeros((64, 1, 4), np.float32), np.zeros((64, 1, 4), np.float32), ts) == KV_POOL_EXHAUSTED
+    assert _same(before, _snapshot(m))

@@ -51,6 +51,10 @@ MUTANTS = {
     "decode_pool_axes_swapped": ("((phys * Hkv + g) * page_size + t % page_size) * D",
                                  "((phys * page_size + t % page_size) * Hkv + g) * D"),
     "decode_drops_newest": ("vseq, n, Hq, Hkv, D, scale,", "vseq, n - 1, Hq, Hkv, D, scale,"),
+    "prefill_sees_whole_sequence": ("kseq, vseq, pos + 1, Hq, Hkv, D, scale,", "kseq, vseq, n, Hq, Hkv, D, scale,"),
+    "prefill_rows_reversed": ("const int64_t row = token_start[s] + j;",
+                              "const int64_t row = token_start[s + 1] - 1 - j;"),
+    "prefill_positions_from_start": ("const int64_t pos = n - n_new + j;", "const int64_t pos = j;"),
 }
 
 
