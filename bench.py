@@ -9,8 +9,9 @@ All inputs are generated once and already resident in HBM when timing starts.
 
 Printed: one JSON line.  `value` is the causal forward+backward rate in
 algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
-QK^T recompute, dV, dP, dK, dQ backward) over the summed event times of the two
-calls; the decode rate (algorithmic HBM bytes per call / call time), the
+QK^T recompute, dV, dP, dK, dQ backward) over the event time from before the
+forward to after the backward (the two calls issued back to back); separate
+breakdown steps with an event between the calls give the per-call times; the decode rate (algorithmic HBM bytes per call / call time), the
 8192-token grouped-query forward and backward, the materialized path, a batched
 paged prefill of a ragged 8-sequence batch and the latency of a K/V append (the
 step before decode) are reported beside it.  Each decode call
@@ -158,23 +159,25 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         attn.attn_causal_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, stream=stream)
-        if ev is not None:
+        if ev is not None and len(ev) == 4:  # breakdown: an event between the two calls
             ev[1].record(stream)
         attn.attn_causal_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq=dq, dk=dk, dv=dv, workspace=ws,
                              stream=stream)
         if ev is not None:
-            ev[2].record(stream)
+            ev[-2].record(stream)
         if args.only == "all":
             kp, vp = pools[i % len(pools)]
             attn.attn_paged_decode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
         if ev is not None:
-            ev[3].record(stream)
+            ev[-1].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed steps: one event before the forward, one after the backward (the pass itself,
+    # back to back as a training step issues it), one after the decode
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, evs[i])
@@ -183,18 +186,27 @@ def main():
     if args.only == "bwd":
         print(json.dumps({"only": "bwd", "steps": args.steps}), flush=True)
         return
-    t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
-    t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
-    t_dec = [e[2].elapsed_time(e[3]) for e in evs]
-    t_step = [e[0].elapsed_time(e[3]) for e in evs]
-    sum_fwd, sum_bwd = sum(t_fwd), sum(t_bwd)
+    t_fb = [e[0].elapsed_time(e[1]) for e in evs]
+    t_dec = [e[1].elapsed_time(e[2]) for e in evs]
+    t_step = [e[0].elapsed_time(e[2]) for e in evs]
     K = args.steps
 
-    # headline: fwd+bwd algorithmic TFLOP/s over the summed event time of the two calls
-    value = (fwd_flops + bwd_flops) * K / ((sum_fwd + sum_bwd) * 1e-3) / 1e12
-    bwd_avg_s = sum_bwd / K * 1e-3
+    # breakdown steps (after the timed ones): an event between the forward and the
+    # backward too, for the per-kernel times and the backward's roofline
+    nb = max(10, K // 2)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    for i in range(nb):
+        step(K + i, bev[i])
+    torch.cuda.synchronize()
+    t_fwd = [e[0].elapsed_time(e[1]) for e in bev]
+    t_bwd = [e[1].elapsed_time(e[2]) for e in bev]
+    sum_fwd, sum_bwd = sum(t_fwd), sum(t_bwd)
+
+    # headline: fwd+bwd algorithmic TFLOP/s over the event time of the two calls
+    value = (fwd_flops + bwd_flops) * K / (sum(t_fb) * 1e-3) / 1e12
+    bwd_avg_s = sum_bwd / nb * 1e-3
     bwd_tflops = bwd_flops / bwd_avg_s / 1e12
-    fwd_avg_s = sum_fwd / K * 1e-3
+    fwd_avg_s = sum_fwd / nb * 1e-3
     dec_avg_s = sum(t_dec) / K * 1e-3
     dec_gbps = dbytes / dec_avg_s / 1e9
 
@@ -329,7 +341,8 @@ def main():
             "avg_launch_us": round(bwd_avg_s * 1e6, 2),
         },
         "fwd_bwd": {
-            "fwd_us": round(fwd_avg_s * 1e6, 2), "bwd_us": round(bwd_avg_s * 1e6, 2),
+            "us": round(sum(t_fb) / K * 1e3, 2), "us_median": round(statistics.median(t_fb) * 1e3, 2),
+            "breakdown_steps": nb, "fwd_us": round(fwd_avg_s * 1e6, 2), "bwd_us": round(bwd_avg_s * 1e6, 2),
             "fwd_tflops": round(fwd_flops / fwd_avg_s / 1e12, 3), "bwd_tflops": round(bwd_tflops, 3),
             "fwd_bwd_tflops": round(value, 3), "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
             "fwd_us_median": round(statistics.median(t_fwd) * 1e3, 2),
