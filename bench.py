@@ -43,7 +43,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 # HBM bytes per attn_causal_bwd launch on the 1024-token workload, from FETCH_SIZE (x2.00)
 # and WRITE_SIZE (x1.00) counter passes; valid only for the kernel source they were taken on.
 BWD_TRAFFIC_BYTES = 164.2e6
-BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "1f5e43d90a40d304"
+BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "a73597ac5ebbbc3d"
 CAUSAL = "mha_b4_h8_t1024_d64"
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"
 DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
