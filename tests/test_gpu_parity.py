@@ -418,3 +418,18 @@ def test_decode_matches_causal_last_row(dev):
     od, lsed = _decode(d, dev)
     assert rel_err(od[0], o[0, :, T - 1]) <= TOL_O
     assert rel_err(lsed[0], lse[0, :, T - 1]) <= TOL_LSE
+
+
+@pytest.mark.parametrize("S,Hkv,G,ctx_hi", [(1, 4, 4, 9000), (3, 8, 2, 3000), (7, 3, 5, 1500), (150, 1, 16, 200)])
+def test_decode_split_layouts(dev, orc, S, Hkv, G, ctx_hi):
+    """Split-path layouts: one long sequence (its groups spread over the whole grid),
+    two columns of KV heads (Hkv = 8), a partial column (Hkv = 3), and many short
+    sequences over one KV head (several 64-sequence chunks of the partition)."""
+    D, ps = 64, 16
+    announce(f"decode split layout S={S} Hkv={Hkv} G={G}")
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=ctx_hi,
+                               max_pages=math.ceil(ctx_hi / ps), seed=500 + S + Hkv)
+    o, lse = _decode(d, dev)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE

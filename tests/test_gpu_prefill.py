@@ -212,3 +212,29 @@ def test_append_tokens_then_prefill(dev, orc, S, Hkv, D, ps, max_pages, num_page
         assert rel_err(o, ro) <= TOL_O and rel_err(lse, rlse) <= TOL_LSE, ("prefill after append", step)
     assert KV_OK in saw
     assert saw & {KV_POOL_EXHAUSTED, KV_SEQUENCE_FULL}, "no refused append was exercised"
+
+
+def test_prefill_many_sequences(dev, orc):
+    """More sequences than one wave's lanes (the block search spans several 64-sequence
+    chunks), with empty ones mixed in."""
+    announce("prefill S=100")
+    rng = np.random.default_rng(90)
+    S = 100
+    cached = rng.integers(0, 200, size=S).tolist()
+    new = rng.integers(0, 70, size=S).tolist()
+    new[5] = 0
+    new[-1] = 1
+    d = _batch(S, 4, 2, 32, 16, cached, new, seed=91)
+    _check(d, dev, orc)
+
+
+def test_append_tokens_nothing_new(dev):
+    """N = 0: every sequence adds no row; the state is unchanged and the status OK."""
+    announce("append_tokens N=0")
+    c = attn.PagedKvCache(3, 2, 16, 16, 2, 4, dev)
+    m = KvCacheModel(3, 2, 16, 16, 2, 4)
+    ts = torch.zeros((4,), dtype=torch.int32, device=dev)
+    empty = torch.zeros((0, 2, 16), device=dev)
+    c.append_tokens(empty, empty, ts)
+    m.append_tokens(np.zeros((0, 2, 16), np.float32), np.zeros((0, 2, 16), np.float32), np.zeros(4, np.int32))
+    _assert_same_state(c, m, "N=0")
