@@ -27,8 +27,8 @@
 //   2. attn_decode_combine: per (sequence, query head), merges the partials with
 //      the log-sum-exp rule M = max m_c, L = sum 2^(m_c - M) l_c,
 //      O = sum 2^(m_c - M) o_c / L.
-// With at least one (sequence, KV head) pair per CU a single fused kernel takes a
-// whole pair per work-group instead.
+// For more sequences than the split's partition holds (1024) a single fused kernel
+// takes a whole (sequence, KV head) pair per work-group instead.
 #include <algorithm>
 
 #include "attn_launch.h"
@@ -249,15 +249,17 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // The split path's partition, computed by every wave on its own from the
 // sequence lengths (no LDS, no barrier): lane l of chunk c stands for sequence
 // s = 64c + l (S <= 64 * NCH) and holds P_{s+1}, the number of 16-position groups
-// of sequences 0..s.  Lengths are clamped to the block table's capacity (and a
+// of sequences 0..s, and the sequence's first partial slot and slot count.  Lengths are clamped to the block table's capacity (and a
 // negative one taken as 0), so a broken length can give wrong numbers but never an
 // out-of-bounds read.
-constexpr int kDecodeScanChunks = 4;  // largest NCH: up to 256 sequences on the split path
+constexpr int kDecodeScanChunks = 16;  // largest NCH: up to 1024 sequences on the split path
 
 template <int NCH>
 struct DecodePartition {
     int incl[NCH];  // P_{s+1} at lane s % 64 of chunk s / 64
     int len[NCH];   // clamped length of sequence s, same places
+    int base[NCH];  // first partial slot of sequence s (exclusive prefix sum of the counts)
+    int cnt[NCH];   // partials of sequence s: the work-groups its groups fall to
     int total;      // P_S
     int nact;       // active work-groups: min(nwg, total)
 
@@ -279,19 +281,42 @@ struct DecodePartition {
         }
         total = wave_uniform(carry);
         nact = min(nwg, total);
-    }
-    // value of a per-sequence register at sequence s (wave-uniform s < 64 * NCH)
-    __device__ __forceinline__ static int at(const int (&v)[NCH], int s) {
-        int x = v[0];
+        // partial slots: sequence s owns cnt_s = owner(P_{s+1} - 1) - owner(P_s) + 1 of them
+        // (0 when empty), consecutive from base_s; there are at most nact + S - 1 in all
+        int carry2 = 0;
 #pragma unroll
-        for (int c = 1; c < NCH; ++c) x = (s >> 6) == c ? v[c] : x;
-        return __builtin_amdgcn_readlane(x, s & 63);
+        for (int c = 0; c < NCH; ++c) {
+            const int pe = incl[c], ps = pe - (len[c] + 15) / 16;
+            cnt[c] = pe > ps ? owner(pe - 1) - owner(ps) + 1 : 0;
+            base[c] = carry2 + wave_incl_scan(cnt[c]) - cnt[c];
+            carry2 = __builtin_amdgcn_readlane(base[c] + cnt[c], 63);
+        }
+    }
+    // value of a per-sequence register at sequence s (wave-uniform s < 64 * NCH); a
+    // cross-lane read, so the whole wave must be active.  Each chunk is read out first
+    // and the scalar results selected, so the arrays stay in registers (a select over
+    // the array elements themselves becomes an indexed per-lane array that the compiler
+    // moves to LDS).
+    __device__ __forceinline__ static int at(const int (&v)[NCH], int s) {
+        int x = __builtin_amdgcn_readlane(v[0], s & 63);
+#pragma unroll
+        for (int c = 1; c < NCH; ++c) {
+            const int y = __builtin_amdgcn_readlane(v[c], s & 63);
+            x = (s >> 6) == c ? y : x;
+        }
+        return x;
     }
     __device__ __forceinline__ int start(int s) const { return s == 0 ? 0 : at(incl, s - 1); }  // P_s
     __device__ __forceinline__ int end(int s) const { return at(incl, s); }                     // P_{s+1}
     __device__ __forceinline__ int length(int s) const { return at(len, s); }
-    // the work-group owning group u: work-group w takes groups [w N / n, (w+1) N / n)
-    __device__ __forceinline__ int owner(int u) const { return (int)((((int64_t)u + 1) * nact - 1) / total); }
+    __device__ __forceinline__ int first_slot(int s) const { return at(base, s); }
+    __device__ __forceinline__ int slots(int s) const { return at(cnt, s); }
+    // the work-group owning group u (total > 0): work-group w takes groups [w N / n, (w+1) N / n)
+    __device__ __forceinline__ int owner(int u) const {
+        if ((int64_t)total * nact < ((int64_t)1 << 31))  // wave-uniform: 32-bit when it cannot overflow
+            return (int)(((uint32_t)(u + 1) * (uint32_t)nact - 1u) / (uint32_t)total);
+        return (int)((((int64_t)u + 1) * nact - 1) / total);
+    }
     // sequences that end at or before group u
     __device__ __forceinline__ int ended_by(int u, int S) const {
         const int lane = threadIdx.x & 63;
@@ -308,16 +333,17 @@ struct DecodePartition {
 // work-group streams the same number of K/V bytes to within one group, whatever the
 // mix of context lengths.  A range may start or end inside a sequence and may cover
 // several: for each sequence it touches the work-group writes one partial (m, l, o) of
-// every query head of its KV heads, into slot k = w - owner(first group of the
-// sequence) of that sequence (k < kcap: a sequence spans at most min(n, its group
-// count) work-groups).  The waves of a work-group are neighbouring KV heads of the
-// same positions, so a page is read contiguously.
+// every query head of its KV heads, into slot base_s + (w - owner(first group of s)):
+// a sequence's partials are consecutive and there are at most n + S - 1 in all.  The
+// work-group owning a sequence's first group records its first slot and slot count
+// for the merge.  The waves of a work-group are neighbouring KV heads of the same
+// positions, so a page is read contiguously.
 template <int D, int DEPTH, int NCH>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     const float* __restrict__ Qd, const float* __restrict__ Kp, const float* __restrict__ Vp,
     const int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, float* __restrict__ Po,
-    float* __restrict__ Pm, float* __restrict__ Pl, int32_t* __restrict__ Cnt, int S, int Hq, int Hkv, int PS,
-    int max_pages, int num_pages, int nwg, int kcap, float c2 /* scale * log2(e) */) {
+    float* __restrict__ Pm, float* __restrict__ Pl, int32_t* __restrict__ Meta, int S, int Hq, int Hkv, int PS,
+    int max_pages, int num_pages, int nwg, float c2 /* scale * log2(e) */) {
     using Tr = DecTraits<D>;
     const int w = wave_uniform(threadIdx.x >> 6);
     const int kvh = blockIdx.y * (blockDim.x >> 6) + w;
@@ -355,10 +381,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 
         // partial: head h = 4g + r lives in lanes (g, *), register r; head li's l in lanes (*, li)
         const float lt = rows4_sum(l);
-        const int k = wg - pt.owner(ps);  // this partial's slot among the sequence's
-        if (k == 0 && kvh == blockIdx.y * (blockDim.x >> 6) && lane == 0)  // one writer per (sequence, column)
-            Cnt[(size_t)blockIdx.y * S + s] = pe > ps ? pt.owner(pe - 1) - pt.owner(ps) + 1 : 0;
-        const size_t slot = (size_t)s * kcap + k;
+        const int k = wg - pt.owner(ps);  // this partial's place among the sequence's
+        const int first = wave_uniform(pt.first_slot(s));
+        const int nslots = wave_uniform(pt.slots(s));  // read with the whole wave active
+        if (k == 0 && blockIdx.y == 0 && w == 0 && lane == 0) {  // one writer per sequence
+            Meta[2 * s] = first;
+            Meta[2 * s + 1] = nslots;
+        }
+        const size_t slot = (size_t)(first + k);
         const size_t hb = slot * Hq + (size_t)kvh * G;  // row of query head kvh * G
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -387,42 +417,40 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 // log-sum-exp rule M = max m_c, L = sum 2^(m_c - M) l_c, O = sum 2^(m_c - M) o_c / L,
 // 64 partials per pass with a running (M, L, o): lane c holds partial c's statistics,
 // the weight of partial c reaches every lane by a lane read, and the lanes sweep the
-// head dim (dims lane and lane + 64).  The sequence's partials sit in fixed slots, so
-// the first pass's loads go out together with the load of their count; slots past the
-// count are masked by selects.
+// head dim (dims lane and lane + 64).  The sequence's first slot and slot count come
+// first (one load), then the partials.
 constexpr int kCombineBatch = 16;  // partial rows loaded together
 
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const float* __restrict__ Po, const float* __restrict__ Pm, const float* __restrict__ Pl,
-    const int32_t* __restrict__ Cnt, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int Hkv, int D,
-    int kcap) {
+    const int32_t* __restrict__ Meta, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int D,
+    int nslots) {
     const int lane = threadIdx.x;
     const int s = blockIdx.x / Hq;
     const int h = blockIdx.x % Hq;
-    const int col = h / (Hq / Hkv) / kDecodeWaves;  // column of KV heads that wrote this head
-    const size_t first = (size_t)s * kcap;
+    // clamped to the workspace: a sequence without positions (outside the documented
+    // domain) has no writer, and its output is then unspecified but its reads stay in bounds
+    const int first = min(max(wave_uniform(Meta[2 * s]), 0), nslots);
+    const int n = min(max(wave_uniform(Meta[2 * s + 1]), 0), nslots - first);
     const bool d0 = lane < D, d1 = lane + 64 < D;
-    const int n_ld = Cnt[(size_t)col * S + s];
     float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
-    for (int c0 = 0; c0 < kcap; c0 += 64) {
+    for (int c0 = 0; c0 < n; c0 += 64) {
         const int c = c0 + lane;
-        const int cn = min(64, kcap - c0);  // slots of this pass
-        const size_t row = (first + c0 + min(lane, cn - 1)) * Hq + h;
+        const bool valid = c < n;
+        const size_t row = (size_t)(first + (valid ? c : c0)) * Hq + h;
         const float pm_ld = Pm[row], pl_ld = Pl[row];  // unconditional loads, masked below
+        const int cv = min(64, n - c0);                // partials of this pass
         float x0[kCombineBatch], x1[kCombineBatch];
         auto load = [&](int cb) {
 #pragma unroll
             for (int j = 0; j < kCombineBatch; ++j) {
-                const float* src = Po + ((first + c0 + min(cb + j, cn - 1)) * Hq + h) * D;
+                const float* src = Po + ((size_t)(first + c0 + min(cb + j, cv - 1)) * Hq + h) * D;
                 const float y0 = src[min(lane, D - 1)], y1 = src[min(lane + 64, D - 1)];
                 x0[j] = d0 ? y0 : 0.f;
                 x1[j] = d1 ? y1 : 0.f;
             }
         };
         load(0);
-        const int n = wave_uniform(n_ld);  // the sequence's partial count
-        if (c0 >= n) break;                // wave-uniform
-        const bool valid = c < n;
         const float pm = valid ? pm_ld : -INFINITY;
         const float m_new = fmaxf(M, wave_max(pm));  // finite: partial c0 exists
         const float keep = exp2_hw(M - m_new);        // 0 on the first pass
@@ -431,7 +459,6 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
         acc0 *= keep;
         acc1 *= keep;
         M = m_new;
-        const int cv = min(64, n - c0);  // valid partials of this pass
         for (int cb = 0; cb < cv; cb += kCombineBatch) {
             if (cb > 0) load(cb);
 #pragma unroll
@@ -442,7 +469,6 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
                 acc1 += ok ? __int_as_float(wj) * x1[j] : 0.f;
             }
         }
-        if (c0 + 64 >= n) break;  // wave-uniform: no further pass
     }
     const float inv = 1.f / L;
     float* dst = O + ((size_t)s * Hq + h) * D;
@@ -532,51 +558,53 @@ bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group) {
     return d_ok && p_ok && group >= 1 && group <= 16;
 }
 
-// Partial slots per sequence on the split path: a sequence spans at most as many
-// work-groups as it has 16-position groups, and at most the grid.
-static int64_t decode_slots_per_seq(int64_t page_size, int64_t max_pages) {
-    return std::min<int64_t>(kDecodeMaxWgs, (page_size * max_pages + 15) / 16);
-}
-
-// Workspace (floats): o [S][slots][Hq][D], then m and l [S][slots][Hq], then the
-// partial counts [ceil(Hkv / 4)][S] (int32).
+// Workspace (floats): partial slots -- o [slots][Hq][D], then m and l [slots][Hq] -- for
+// at most the grid plus the sequences, then each sequence's first slot and slot count
+// (2 x S int32).
 size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages) {
-    return (size_t)(S * decode_slots_per_seq(page_size, max_pages) * Hq * (D + 2) +
-                    (Hkv + kDecodeWaves - 1) / kDecodeWaves * S);
+    (void)Hkv;
+    (void)page_size;
+    (void)max_pages;
+    return (size_t)((kDecodeMaxWgs + S) * Hq * (D + 2) + 2 * S);
 }
 
 bool decode_split_supported(int64_t S) { return S <= 64 * kDecodeScanChunks; }
+// measured: the balanced split beats one work-group per (sequence, KV head) from 32 up to
+// 256 sequences (e.g. 57.8 vs 71.4 us at 64, 218 vs 246 us at 256 sequences of 512..4096
+// positions), so it is used whenever its partition fits
 
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
-    if (a.S * a.Hkv >= a.cu_count || !decode_split_supported(a.S)) {
-        // At least one (sequence, KV head) pair per CU: one fused kernel.
+    if (!decode_split_supported(a.S)) {
+        // More sequences than the split's partition holds: one fused work-group per
+        // (sequence, KV head).
         hipLaunchKernelGGL((attn_decode_fused_kernel<D>), dim3((unsigned)a.Hkv, (unsigned)a.S),
                            dim3(64 * fused_waves<D>()), 0, stream, a.q, a.k_pool, a.v_pool, a.block_table,
                            a.context_lens, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.page_size,
                            (int)a.max_pages, (int)a.num_pages, a.scale * kLog2e);
         return hipGetLastError();
     }
-    // Few pairs: the positions of all sequences in equal shares over the whole chip, then the merge.
+    // The positions of all sequences in equal shares over the whole chip, then the merge.
     const int wpw = (int)std::min<int64_t>(a.Hkv, kDecodeWaves);  // waves (KV heads) per work-group
     const int gy = (int)((a.Hkv + wpw - 1) / wpw);
     const int nwg = (int)std::max<int64_t>(
         1, std::min<int64_t>(kDecodeMaxWgs, (int64_t)kDecodeWavesPerCu * a.cu_count / (wpw * gy)));
-    const int kcap = (int)decode_slots_per_seq(a.page_size, a.max_pages);
+    const int64_t slots = kDecodeMaxWgs + a.S;
     float* Po = a.partial;
-    float* Pm = Po + (size_t)(a.S * kcap * a.Hq * D);
-    float* Pl = Pm + (size_t)(a.S * kcap * a.Hq);
-    int32_t* Cnt = (int32_t*)(Pl + (size_t)(a.S * kcap * a.Hq));
-    auto split = a.S <= 64 ? attn_decode_split_kernel<D, kDecodeDepth, 1>
-                           : attn_decode_split_kernel<D, kDecodeDepth, kDecodeScanChunks>;
+    float* Pm = Po + (size_t)(slots * a.Hq * D);
+    float* Pl = Pm + (size_t)(slots * a.Hq);
+    int32_t* Meta = (int32_t*)(Pl + (size_t)(slots * a.Hq));
+    auto split = a.S <= 64    ? attn_decode_split_kernel<D, kDecodeDepth, 1>
+                 : a.S <= 256 ? attn_decode_split_kernel<D, kDecodeDepth, 4>
+                              : attn_decode_split_kernel<D, kDecodeDepth, kDecodeScanChunks>;
     hipLaunchKernelGGL(split, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), 0, stream, a.q, a.k_pool, a.v_pool,
-                       a.block_table, a.context_lens, Po, Pm, Pl, Cnt, (int)a.S, (int)a.Hq, (int)a.Hkv,
-                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, kcap, a.scale * kLog2e);
+                       a.block_table, a.context_lens, Po, Pm, Pl, Meta, (int)a.S, (int)a.Hq, (int)a.Hkv,
+                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,
-                       Cnt, a.o, a.lse, (int)a.S, (int)a.Hq, (int)a.Hkv, D, kcap);
+                       Meta, a.o, a.lse, (int)a.S, (int)a.Hq, D, (int)slots);
     return hipGetLastError();
 }
 

@@ -130,7 +130,8 @@ attn_status attn_causal_bwd(const float* q, const float* k, const float* v,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_paged_decode needs for these sizes (0 when a
- * size is invalid). */
+ * size is invalid): partial results of 1024 + S (position range, query head)
+ * pieces and two int32 per sequence, whatever the page size and table width. */
 size_t attn_paged_decode_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                                          int64_t page_size, int64_t max_pages_per_seq);
 

@@ -67,11 +67,10 @@ def test_workspace_queries(L):
     assert attn.attn_causal_bwd_workspace_bytes(1, 2, 2, 16, 8) == 256  # rounded up to 256
     assert attn.attn_causal_bwd_workspace_bytes(1, 3, 2, 16, 8) == 0    # Hq % Hkv != 0
     assert attn.attn_causal_bwd_workspace_bytes(0, 2, 2, 16, 8) == 0
-    # partial (m, l, o[D]) records per sequence and query head for min(1024, capacity / 16)
-    # slots (a sequence spans at most that many work-groups) and one int per sequence and
-    # column of 4 KV heads, 256-byte rounded
+    # partial (m, l, o[D]) records per query head for 1024 + S slots (the split grid plus
+    # one boundary per sequence) and a first slot and slot count per sequence, 256-byte rounded
     def expect(S, Hq, Hkv, D, ps, maxp):
-        b = S * min(1024, -(-ps * maxp // 16)) * Hq * (D + 2) * 4 + -(-Hkv // 4) * S * 4
+        b = (1024 + S) * Hq * (D + 2) * 4 + 2 * S * 4
         return -(-b // 256) * 256
     for args in ((32, 16, 4, 64, 16, 256), (32, 16, 4, 64, 16, 512), (32, 16, 4, 64, 16, 1),
                  (32, 16, 4, 64, 16, 100000), (3, 8, 8, 32, 64, 7), (1, 1, 1, 8, 16, 1)):

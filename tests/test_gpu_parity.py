@@ -338,11 +338,13 @@ DECODE_CASES = [(D, G, ps) for D in (8, 16, 32, 64, 128) for G in (1, 4) for ps 
 DECODE_CASES += [(64, 8, 16), (32, 2, 32), (16, 8, 32)]
 
 
+DECODE_SPLIT_MAX_S = 1024  # the split path's partition holds up to this many sequences
+
+
 def _decode_batch(dev, path, Hkv):
-    """Sequences per batch that select the split (few (sequence, KV head) pairs) or
-    the fused (at least half a CU count of pairs) decode path."""
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    return 5 if path == "split" else -(-cus // (2 * Hkv)) + 1
+    """Sequences per batch that select the split (at most 1024 sequences) or the
+    fused (more) decode path."""
+    return 5 if path == "split" else DECODE_SPLIT_MAX_S + 1
 
 
 @pytest.mark.parametrize("path", ["split", "fused"])
@@ -351,8 +353,10 @@ def test_decode_shapes(dev, orc, D, G, ps, path):
     Hkv = 2
     S = _decode_batch(dev, path, Hkv)
     announce(f"decode {path} S={S} D={D} G={G} page={ps}")
-    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=520,
+    hi = 520 if path == "split" else 160  # the fused batch is 205 times larger
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=hi,
                                max_pages=math.ceil(520 / ps) + 1, seed=100 + D + G + ps)
+    d["context_lens"][1] = 520  # several 64-group passes of the split path's waves
     d["context_lens"][0] = 1  # a single cached position
     o, lse = _decode(d, dev)
     ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
@@ -372,8 +376,8 @@ def test_decode_long_context(dev, orc, path):
     Hkv, G, D, ps = 2, 4, 64, 64
     S = _decode_batch(dev, path, Hkv)
     announce(f"decode long context {path} S={S}")
-    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=9000,
-                               max_pages=math.ceil(9000 / ps), seed=77)
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1,
+                               ctx_hi=9000 if path == "split" else 200, max_pages=math.ceil(9000 / ps), seed=77)
     d["context_lens"][0] = 9000
     d["context_lens"][1] = 8193
     o, lse = _decode(d, dev)
@@ -420,11 +424,14 @@ def test_decode_matches_causal_last_row(dev):
     assert rel_err(lsed[0], lse[0, :, T - 1]) <= TOL_LSE
 
 
-@pytest.mark.parametrize("S,Hkv,G,ctx_hi", [(1, 4, 4, 9000), (3, 8, 2, 3000), (7, 3, 5, 1500), (150, 1, 16, 200)])
+@pytest.mark.parametrize("S,Hkv,G,ctx_hi", [(1, 4, 4, 9000), (3, 8, 2, 3000), (7, 3, 5, 1500), (150, 1, 16, 200),
+                                            (700, 1, 4, 120), (1024, 2, 4, 64), (1024, 8, 1, 40)])
 def test_decode_split_layouts(dev, orc, S, Hkv, G, ctx_hi):
     """Split-path layouts: one long sequence (its groups spread over the whole grid),
-    two columns of KV heads (Hkv = 8), a partial column (Hkv = 3), and many short
-    sequences over one KV head (several 64-sequence chunks of the partition)."""
+    two columns of KV heads (Hkv = 8), a partial column (Hkv = 3), many short
+    sequences over one KV head (several 64-sequence chunks of the partition), and
+    up to the largest batch the split path takes (1024 sequences: more sequences than
+    work-groups, so a work-group holds partials of several sequences)."""
     D, ps = 64, 16
     announce(f"decode split layout S={S} Hkv={Hkv} G={G}")
     d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=ctx_hi,
