@@ -11,8 +11,10 @@ Printed: one JSON line.  `value` is the causal forward+backward rate in
 algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
 QK^T recompute, dV, dP, dK, dQ backward) over the event time from before the
 forward to after the backward (the two calls issued back to back); separate
-breakdown steps with an event between the calls give the per-call times; the decode rate (algorithmic HBM bytes per call / call time), the
-8192-token grouped-query forward and backward, the materialized path, a batched
+breakdown steps with an event between the calls give the per-call times.  The
+decode rate is the algorithmic HBM bytes per call over the average time of
+back-to-back decode calls between two events (the step's decode call, event to
+event, is reported beside it).  The 8192-token grouped-query forward and backward, the materialized path, a batched
 paged prefill of a ragged 8-sequence batch and the latency of a K/V append (the
 step before decode) are reported beside it.  Each decode call
 reads a different one of several pool replicas so the 256 MB last-level cache
@@ -207,7 +209,22 @@ def main():
     bwd_avg_s = sum_bwd / nb * 1e-3
     bwd_tflops = bwd_flops / bwd_avg_s / 1e12
     fwd_avg_s = sum_fwd / nb * 1e-3
-    dec_avg_s = sum(t_dec) / K * 1e-3
+    # decode on its own: back-to-back calls between two events (each on the next pool
+    # replica), so that no event marker sits between the calls; the in-step time above
+    # (event after the backward to event after the decode) is reported beside it
+    nd = max(20, 2 * K) if args.only == "all" else 0
+    if nd:
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(nd):
+            kp, vp = pools[i % len(pools)]
+            attn.attn_paged_decode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dec_avg_s = d0.elapsed_time(d1) / nd * 1e-3
+    else:
+        dec_avg_s = sum(t_dec) / K * 1e-3
+    dec_step_s = sum(t_dec) / K * 1e-3
     dec_gbps = dbytes / dec_avg_s / 1e9
 
     # the 8192-token grouped-query forward (O + LSE), timed separately, then its
@@ -349,7 +366,8 @@ def main():
             "bwd_us_median": round(statistics.median(t_bwd) * 1e3, 2),
         },
         "decode": {
-            "us": round(dec_avg_s * 1e6, 2), "us_median": round(statistics.median(t_dec) * 1e3, 2),
+            "us": round(dec_avg_s * 1e6, 2), "calls_back_to_back": nd,
+            "us_in_step": round(dec_step_s * 1e6, 2), "us_in_step_median": round(statistics.median(t_dec) * 1e3, 2),
             "bytes_per_call": dbytes, "gbps": round(dec_gbps, 1),
             "frac_of_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4), "pool_replicas": len(pools),
         },

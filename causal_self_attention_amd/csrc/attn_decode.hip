@@ -415,16 +415,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 
 // One wave per (sequence, query head) merges the sequence's partials with the
 // log-sum-exp rule M = max m_c, L = sum 2^(m_c - M) l_c, O = sum 2^(m_c - M) o_c / L,
-// 64 partials per pass with a running (M, L, o): lane c holds partial c's statistics,
-// the weight of partial c reaches every lane by a lane read, and the lanes sweep the
-// head dim (dims lane and lane + 64).  The sequence's first slot and slot count come
-// first (one load), then the partials.
-constexpr int kCombineBatch = 16;  // partial rows loaded together
-
+// 64 partials per pass with a running (M, L, o).  The sequence's first slot and slot
+// count come first (one load); then a pass issues all its loads at once: lane c holds
+// partial c's (m, l), and the partial rows are read as float4 pieces, D/4 lanes to a
+// row, so that 64 rows take 64 / (64 / (D/4)) loads per lane.  Each lane weights its
+// rows (the weight of partial c fetched from lane c) and the lanes holding the same
+// head-dim piece are summed at the end.
+template <int D>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const float* __restrict__ Po, const float* __restrict__ Pm, const float* __restrict__ Pl,
-    const int32_t* __restrict__ Meta, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int D,
-    int nslots) {
+    const int32_t* __restrict__ Meta, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int nslots) {
+    constexpr int LPR = D / 4;     // lanes per partial row
+    constexpr int RPI = 64 / LPR;  // rows per load instruction
+    constexpr int NLD = 64 / RPI;  // load instructions per pass of 64 rows
     const int lane = threadIdx.x;
     const int s = blockIdx.x / Hq;
     const int h = blockIdx.x % Hq;
@@ -432,48 +435,38 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     // domain) has no writer, and its output is then unspecified but its reads stay in bounds
     const int first = min(max(wave_uniform(Meta[2 * s]), 0), nslots);
     const int n = min(max(wave_uniform(Meta[2 * s + 1]), 0), nslots - first);
-    const bool d0 = lane < D, d1 = lane + 64 < D;
-    float M = -INFINITY, L = 0.f, acc0 = 0.f, acc1 = 0.f;
+    const int rsub = lane / LPR;       // row of this lane within a load instruction
+    const int col = (lane % LPR) * 4;  // head-dim piece of this lane
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < n; c0 += 64) {
-        const int c = c0 + lane;
-        const bool valid = c < n;
-        const size_t row = (size_t)(first + (valid ? c : c0)) * Hq + h;
-        const float pm_ld = Pm[row], pl_ld = Pl[row];  // unconditional loads, masked below
-        const int cv = min(64, n - c0);                // partials of this pass
-        float x0[kCombineBatch], x1[kCombineBatch];
-        auto load = [&](int cb) {
+        const int cv = min(64, n - c0);  // partials of this pass
+        const size_t stat = (size_t)(first + c0 + min(lane, cv - 1)) * Hq + h;
+        const float pm_ld = Pm[stat], pl_ld = Pl[stat];  // unconditional loads, masked below
+        f32x4 x[NLD];
 #pragma unroll
-            for (int j = 0; j < kCombineBatch; ++j) {
-                const float* src = Po + ((size_t)(first + c0 + min(cb + j, cv - 1)) * Hq + h) * D;
-                const float y0 = src[min(lane, D - 1)], y1 = src[min(lane + 64, D - 1)];
-                x0[j] = d0 ? y0 : 0.f;
-                x1[j] = d1 ? y1 : 0.f;
-            }
-        };
-        load(0);
+        for (int j = 0; j < NLD; ++j)
+            x[j] = *(const f32x4*)(Po + ((size_t)(first + c0 + min(j * RPI + rsub, cv - 1)) * Hq + h) * D + col);
+        const bool valid = lane < cv;
         const float pm = valid ? pm_ld : -INFINITY;
         const float m_new = fmaxf(M, wave_max(pm));  // finite: partial c0 exists
         const float keep = exp2_hw(M - m_new);        // 0 on the first pass
         const float wl = valid ? exp2_hw(pm - m_new) : 0.f;
         L = L * keep + wave_sum(valid ? wl * pl_ld : 0.f);
-        acc0 *= keep;
-        acc1 *= keep;
+        acc *= keep;
         M = m_new;
-        for (int cb = 0; cb < cv; cb += kCombineBatch) {
-            if (cb > 0) load(cb);
 #pragma unroll
-            for (int j = 0; j < kCombineBatch; ++j) {
-                const float wj = __builtin_amdgcn_readlane(__float_as_int(wl), min(cb + j, 63));
-                const bool ok = cb + j < cv;
-                acc0 += ok ? __int_as_float(wj) * x0[j] : 0.f;
-                acc1 += ok ? __int_as_float(wj) * x1[j] : 0.f;
-            }
-        }
+        for (int j = 0; j < NLD; ++j) acc += __shfl(wl, j * RPI + rsub) * x[j];  // weight 0 past cv
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        acc[0] += __shfl_xor(acc[0], off);
+        acc[1] += __shfl_xor(acc[1], off);
+        acc[2] += __shfl_xor(acc[2], off);
+        acc[3] += __shfl_xor(acc[3], off);
     }
     const float inv = 1.f / L;
-    float* dst = O + ((size_t)s * Hq + h) * D;
-    if (d0) dst[lane] = acc0 * inv;
-    if (d1) dst[lane + 64] = acc1 * inv;
+    if (lane < LPR) *(f32x4*)(O + ((size_t)s * Hq + h) * D + col) = acc * inv;
     if (LSE && lane == 0) LSE[(size_t)s * Hq + h] = (M + log2_hw(L)) * kLn2;
 }
 
@@ -603,8 +596,8 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
                        (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_decode_combine_kernel, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,
-                       Meta, a.o, a.lse, (int)a.S, (int)a.Hq, D, (int)slots);
+    hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,
+                       Meta, a.o, a.lse, (int)a.S, (int)a.Hq, (int)slots);
     return hipGetLastError();
 }
 
