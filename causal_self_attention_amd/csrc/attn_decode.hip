@@ -317,6 +317,14 @@ struct DecodePartition {
             return (int)(((uint32_t)(u + 1) * (uint32_t)nact - 1u) / (uint32_t)total);
         return (int)((((int64_t)u + 1) * nact - 1) / total);
     }
+    // Writes each sequence's (first group, length, first slot, slot count) to part[s],
+    // so that a wave can drop the per-lane arrays and read one record per sequence.
+    __device__ __forceinline__ void store(int4* part, int S) const {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            if (64 * c + lane < S) part[64 * c + lane] = make_int4(incl[c] - (len[c] + 15) / 16, len[c], base[c], cnt[c]);
+    }
     // sequences that end at or before group u
     __device__ __forceinline__ int ended_by(int u, int S) const {
         const int lane = threadIdx.x & 63;
@@ -409,6 +417,249 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
         if (g == 0 && li < G) {
             Pm[hb + li] = m;
             Pl[hb + li] = lt;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split path for up to 8 query heads per KV head, on the vector ALUs.  A cached
+// position costs 4 G D flops for 8 D bytes of K and V, i.e. G / 2 flops per byte:
+// at G <= 8 the VALU keeps up with HBM with room to spare, while a 16x16x4 MFMA
+// tile would pad the G heads to 16 columns and spend most of its cycles on zeros.
+// Layout (ND = D / 8 lanes per position, NP = 64 / ND positions per step):
+//   lane = dq + ND * pl owns head dims 4dq .. 4dq+3 and D/2 + 4dq .. D/2 + 4dq+3 of
+//   position pl of the step, so each of its two float4 loads covers ND * 16
+//   contiguous bytes of a position row together with the other dq lanes;
+//   score of head h: 8 FMAs, then a DPP sum over the ND lanes of the position;
+//   softmax: every lane keeps its own running max and sum over the positions it
+//   sees (pl, pl + NP, ...), so the loop needs no other cross-lane step; the max
+//   moves only when a score exceeds it by more than 2^8 (a rare wave-wide branch);
+//   O += p V: 8 FMAs per head into the lane's own dims;
+//   at the end of a sequence's share the NP position lanes are merged with the
+//   log-sum-exp rule and the share is written as one partial per query head.
+template <int D, int GM>
+struct DecValuTraits {
+    static constexpr int ND = D / 8;    // lanes per position
+    static constexpr int NP = 64 / ND;  // positions per step
+    // steps in the K/V register ring: one 16-position group (at least two steps);
+    // measured at the 32-, 128- and 1024-sequence batches, deeper rings and more waves
+    // per CU were slower (the memory system is already saturated by one group ahead)
+    static constexpr int DEPTH = 16 / NP > 2 ? 16 / NP : 2;
+};
+constexpr float kDecodeNoMax = -1e30f;  // running max before any position: finite, so no inf - inf
+
+// sum over the ND lanes of a position (the low lane bits)
+template <int ND>
+__device__ __forceinline__ float sum_dims(float x) {
+    if constexpr (ND >= 2) x += dpp_mov<kDppXor1>(x);
+    if constexpr (ND >= 4) x += dpp_mov<kDppXor2>(x);
+    if constexpr (ND >= 8) x += dpp_mov<kDppHalfMirror>(x);  // the other quad of the half-row
+    if constexpr (ND >= 16) x += dpp_mov<kDppRor8>(x);       // the other half of the row
+    return x;
+}
+// sum / max over the positions of a step (the lane bits above the ND lanes)
+template <int ND>
+__device__ __forceinline__ float sum_positions(float x) {
+    if constexpr (ND == 1) return wave_sum(x);
+    if constexpr (ND == 2) return rows4_sum(row_stride4_sum(x + dpp_mov<kDppXor2>(x)));
+    if constexpr (ND == 4) return rows4_sum(row_stride4_sum(x));
+    if constexpr (ND == 8) return rows4_sum(x + dpp_mov<kDppRor8>(x));
+    return rows4_sum(x);
+}
+template <int ND>
+__device__ __forceinline__ float max_positions(float x) {
+    if constexpr (ND == 1) return wave_max(x);
+    if constexpr (ND == 2) return rows4_max(row_stride4_max(fmaxf(x, dpp_mov<kDppXor2>(x))));
+    if constexpr (ND == 4) return rows4_max(row_stride4_max(x));
+    if constexpr (ND == 8) return rows4_max(fmaxf(x, dpp_mov<kDppRor8>(x)));
+    return rows4_max(x);
+}
+
+// One wave's pass over positions [t_lo, t_hi) of one (sequence, KV head), t_lo a
+// multiple of 16 and t_hi - t_lo <= 1024: bt_lane holds the page of group j of the
+// span in lane j.  K/V loads run DEPTH - 1 steps ahead through a register ring and
+// are issued unconditionally (a step past the span re-reads its last position);
+// lanes past t_hi score -inf and their V is zeroed, so pool slots past the context
+// may hold anything.
+template <int D, int GM>
+__device__ __forceinline__ void decode_valu_span(const float* __restrict__ Kp, const float* __restrict__ Vp,
+                                                 int bt_lane, int Hkv, int kvh, int PS, int t_lo, int t_hi,
+                                                 const float (&q)[GM][8], float (&m)[GM], float (&l)[GM],
+                                                 float (&acc)[GM][8]) {
+    using Tr = DecValuTraits<D, GM>;
+    constexpr int ND = Tr::ND, NP = Tr::NP, DEPTH = Tr::DEPTH;
+    const int lane = threadIdx.x & 63;
+    const int dq = lane % ND;
+    const int pl = lane / ND;
+    const int nsteps = (t_hi - t_lo + NP - 1) / NP;
+    float kr[DEPTH][8], vr[DEPTH][8];
+    auto issue = [&](int k, int slot) {
+        const int t0 = t_lo + min(k, nsteps - 1) * NP;
+        const int t = min(t0 + pl, t_hi - 1);
+        int page;
+        if constexpr (NP <= 16) page = __builtin_amdgcn_readlane(bt_lane, (t0 - t_lo) >> 4);  // one group per step
+        else page = __shfl(bt_lane, (t - t_lo) >> 4);
+        const size_t off = (((size_t)page * Hkv + kvh) * PS + (t & (PS - 1))) * D + 4 * dq;
+        load_vec<4, true>(Kp + off, &kr[slot][0]);
+        load_vec<4, true>(Kp + off + D / 2, &kr[slot][4]);
+        load_vec<4, true>(Vp + off, &vr[slot][0]);
+        load_vec<4, true>(Vp + off + D / 2, &vr[slot][4]);
+    };
+    auto step = [&](int k, int slot) {
+        const bool valid = t_lo + k * NP + pl < t_hi;
+        float sc[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x = fmaf(kr[slot][i], q[h][i], x);
+            x = sum_dims<ND>(x);
+            sc[h] = valid ? x : -INFINITY;
+        }
+        bool need = false;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) need |= sc[h] > m[h] + kLazyRescale;
+        if (__ballot(need)) {  // wave-uniform and rare: move the max of every lane to its max seen
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                const float mn = fmaxf(m[h], sc[h]);
+                const float al = exp2_hw(m[h] - mn);
+                m[h] = mn;
+                l[h] *= al;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+            }
+        }
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = valid ? vr[slot][i] : 0.f;
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float p = exp2_hw(sc[h] - m[h]);  // 0 past the span
+            l[h] += p;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(p, v[i], acc[h][i]);
+        }
+    };
+    // Whole rounds of DEPTH steps, so the loop body has no branch around a step (the
+    // steps past the span are fully masked), and a scheduling barrier after each issue,
+    // so the loads leave in slot order: the compiler's load-count waits are then per
+    // ring slot, the same on loop entry as on the back edge (with the prologue's loads
+    // reordered, the entry state forced a wait for every older load into the loop).
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) {
+        issue(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int k0 = 0; k0 < nsteps; k0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            issue(k0 + d + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+            __builtin_amdgcn_sched_barrier(0);
+            step(k0 + d, d);
+        }
+    }
+}
+
+// The split kernel for G <= GM query heads per KV head (GM = 1, 2, 4 or 8): the same
+// partition, grid and partial slots as the MFMA split kernel above; each wave keeps
+// its copy of the per-sequence records in its own LDS area.
+template <int D, int GM, int NCH>
+__global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
+    const float* __restrict__ Qd, const float* __restrict__ Kp, const float* __restrict__ Vp,
+    const int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, float* __restrict__ Po,
+    float* __restrict__ Pm, float* __restrict__ Pl, int32_t* __restrict__ Meta, int S, int Hq, int Hkv, int PS,
+    int max_pages, int num_pages, int nwg, float c2 /* scale * log2(e) */) {
+    using Tr = DecValuTraits<D, GM>;
+    constexpr int ND = Tr::ND;
+    extern __shared__ int4 dec_seq_info[];  // [waves][64 * NCH]
+    const int w = wave_uniform(threadIdx.x >> 6);
+    const int kvh = blockIdx.y * (blockDim.x >> 6) + w;
+    if (kvh >= Hkv) return;  // wave-uniform; the kernel has no barrier
+    int4* part = dec_seq_info + w * 64 * NCH;
+    DecodePartition<NCH> pt;
+    pt.load(CTX, S);
+    pt.scan(S, PS * max_pages, nwg);
+    const int wg = blockIdx.x;
+    if (wg >= pt.nact) return;
+    const int u_lo = wave_uniform((int)(((int64_t)wg * pt.total) / pt.nact));
+    const int u_hi = wave_uniform((int)(((int64_t)(wg + 1) * pt.total) / pt.nact));
+    const int s_first = wave_uniform(pt.ended_by(u_lo, S));
+    pt.store(part, S);
+    const int lane = threadIdx.x & 63;
+    const int dq = lane % ND;
+    const int pl = lane / ND;
+    const int G = Hq / Hkv;
+    for (int s = s_first; s < S; ++s) {
+        const int4 info = part[s];
+        const int ps = wave_uniform(info.x);
+        const int len = wave_uniform(info.y);
+        const int pe = ps + (len + 15) / 16;
+        if (ps >= u_hi) break;
+        const int a = max(ps, u_lo), e = min(pe, u_hi);
+        if (a >= e) continue;  // a sequence without positions
+        const int32_t* bt_row = BT + (size_t)s * max_pages;
+        int bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, a - ps, 1, min(64, e - a));
+        float q[GM][8];  // query heads kvh*G + h (zero for h >= G), scaled by c2
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float* qr = Qd + ((size_t)s * Hq + (size_t)kvh * G + min(h, G - 1)) * D + 4 * dq;
+            const f32x4 x0 = *(const f32x4*)qr;
+            const f32x4 x1 = *(const f32x4*)(qr + D / 2);
+            const float f = h < G ? c2 : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q[h][i] = x0[i] * f;
+                q[h][4 + i] = x1[i] * f;
+            }
+        }
+        float m[GM], l[GM], acc[GM][8];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            m[h] = kDecodeNoMax;
+            l[h] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+        }
+        for (int j0 = a - ps; j0 < e - ps; j0 += 64) {  // spans of at most 64 groups (one table load each)
+            if (j0 > a - ps) bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, j0, 1, min(64, e - ps - j0));
+            decode_valu_span<D, GM>(Kp, Vp, bt, Hkv, kvh, PS, 16 * j0, min(16 * min(j0 + 64, e - ps), len), q, m,
+                                    l, acc);
+        }
+        // merge the position lanes: M = max m, L = sum 2^(m - M) l, o = sum 2^(m - M) o
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            const float M = max_positions<ND>(m[h]);
+            const float f = exp2_hw(m[h] - M);  // 0 for a lane that saw no position
+            l[h] = sum_positions<ND>(l[h] * f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = sum_positions<ND>(acc[h][i] * f);
+            m[h] = M;
+        }
+        const int k = wg - pt.owner(ps);  // this partial's place among the sequence's
+        const int first = wave_uniform(info.z);
+        const int nslots = wave_uniform(info.w);
+        if (k == 0 && blockIdx.y == 0 && w == 0 && lane == 0) {  // one writer per sequence
+            Meta[2 * s] = first;
+            Meta[2 * s + 1] = nslots;
+        }
+        const size_t hb = (size_t)(first + k) * Hq + (size_t)kvh * G;  // row of query head kvh * G
+        if (pl == 0) {
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                if (h < G) {
+                    float* dst = Po + (hb + h) * D + 4 * dq;
+                    *(f32x4*)dst = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
+                    *(f32x4*)(dst + D / 2) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+            if (h < G && lane == h) {
+                Pm[hb + h] = m[h];
+                Pl[hb + h] = l[h];
+            }
         }
     }
 }
@@ -588,12 +839,30 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     float* Pm = Po + (size_t)(slots * a.Hq * D);
     float* Pl = Pm + (size_t)(slots * a.Hq);
     int32_t* Meta = (int32_t*)(Pl + (size_t)(slots * a.Hq));
-    auto split = a.S <= 64    ? attn_decode_split_kernel<D, kDecodeDepth, 1>
-                 : a.S <= 256 ? attn_decode_split_kernel<D, kDecodeDepth, 4>
-                              : attn_decode_split_kernel<D, kDecodeDepth, kDecodeScanChunks>;
-    hipLaunchKernelGGL(split, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), 0, stream, a.q, a.k_pool, a.v_pool,
-                       a.block_table, a.context_lens, Po, Pm, Pl, Meta, (int)a.S, (int)a.Hq, (int)a.Hkv,
-                       (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, a.scale * kLog2e);
+    const int64_t G = a.Hq / a.Hkv;
+    if (G <= 8) {
+        // up to 8 query heads per KV head: the VALU split kernel, instantiated for the
+        // smallest head capacity GM >= G and the partition's chunk count
+        const bool one = a.S <= 64;
+        const int nch = one ? 1 : kDecodeScanChunks;
+        auto pick = [&](auto k1, auto k16) { return one ? k1 : k16; };
+        decltype(&attn_decode_split_valu_kernel<D, 1, 1>) valu =
+            G == 1   ? pick(attn_decode_split_valu_kernel<D, 1, 1>, attn_decode_split_valu_kernel<D, 1, kDecodeScanChunks>)
+            : G == 2 ? pick(attn_decode_split_valu_kernel<D, 2, 1>, attn_decode_split_valu_kernel<D, 2, kDecodeScanChunks>)
+            : G <= 4 ? pick(attn_decode_split_valu_kernel<D, 4, 1>, attn_decode_split_valu_kernel<D, 4, kDecodeScanChunks>)
+                     : pick(attn_decode_split_valu_kernel<D, 8, 1>, attn_decode_split_valu_kernel<D, 8, kDecodeScanChunks>);
+        const size_t lds = (size_t)wpw * 64 * nch * sizeof(int4);
+        hipLaunchKernelGGL(valu, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), lds, stream, a.q, a.k_pool,
+                           a.v_pool, a.block_table, a.context_lens, Po, Pm, Pl, Meta, (int)a.S, (int)a.Hq,
+                           (int)a.Hkv, (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, a.scale * kLog2e);
+    } else {
+        auto split = a.S <= 64    ? attn_decode_split_kernel<D, kDecodeDepth, 1>
+                     : a.S <= 256 ? attn_decode_split_kernel<D, kDecodeDepth, 4>
+                                  : attn_decode_split_kernel<D, kDecodeDepth, kDecodeScanChunks>;
+        hipLaunchKernelGGL(split, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), 0, stream, a.q, a.k_pool,
+                           a.v_pool, a.block_table, a.context_lens, Po, Pm, Pl, Meta, (int)a.S, (int)a.Hq,
+                           (int)a.Hkv, (int)a.page_size, (int)a.max_pages, (int)a.num_pages, nwg, a.scale * kLog2e);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,

@@ -336,6 +336,8 @@ def test_decode_pool_permutation(dev):
 
 DECODE_CASES = [(D, G, ps) for D in (8, 16, 32, 64, 128) for G in (1, 4) for ps in (16, 64)]
 DECODE_CASES += [(64, 8, 16), (32, 2, 32), (16, 8, 32)]
+# more than 8 query heads per KV head: the MFMA split kernel (8 or fewer: the VALU one)
+DECODE_CASES += [(64, 16, 16), (32, 12, 32), (128, 16, 64), (8, 16, 16), (16, 3, 16), (128, 6, 32)]
 
 
 DECODE_SPLIT_MAX_S = 1024  # the split path's partition holds up to this many sequences
