@@ -14,7 +14,9 @@ forward to after the backward (the two calls issued back to back); separate
 breakdown steps with an event between the calls give the per-call times.  The
 decode rate is the algorithmic HBM bytes per call over the average time of
 back-to-back decode calls between two events (the step's decode call, event to
-event, is reported beside it).  The 8192-token grouped-query forward and backward, the materialized path, a batched
+event, is reported beside it); `decode_sweep` adds the same shape with one
+16-position group per sequence (the fixed cost of a call), a 256-sequence batch,
+and the workload's rate beyond that fixed cost.  The 8192-token grouped-query forward and backward, the materialized path, a batched
 paged prefill of a ragged 8-sequence batch and the latency of a K/V append (the
 step before decode) are reported beside it.  Each decode call
 reads a different one of several pool replicas so the 256 MB last-level cache
@@ -282,6 +284,44 @@ def main():
     p_bytes = B * Hq * T * T * 4
     del mp, mdq, mdk, mdv
 
+    # decode cost structure: the workload's shape with one 16-position group per sequence
+    # (what a call costs besides streaming K/V) and a 256-sequence batch with the
+    # workload's length distribution, each timed back to back like the decode above
+    def decode_back_to_back(d, reps, calls=20):
+        q2, bt2, ctx2 = d["q"].to(dev), d["block_table"].to(dev), d["context_lens"].to(dev)
+        pools2 = [(d["k_pool"].to(dev), d["v_pool"].to(dev)) for _ in range(reps)]
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty(q2.shape[:2], device=dev)
+        ws2 = torch.empty((attn.attn_paged_decode_workspace_bytes(q2.shape[0], dcfg["Hq"], dcfg["Hkv"], dcfg["D"],
+                                                                  dcfg["page_size"], bt2.shape[1]) // 4,),
+                          device=dev)
+        for i in range(3):
+            attn.attn_paged_decode(q2, *pools2[i % reps], bt2, ctx2, o=o2, lse=l2, workspace=ws2, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(calls):
+            attn.attn_paged_decode(q2, *pools2[i % reps], bt2, ctx2, o=o2, lse=l2, workspace=ws2, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls * 1e3, decode_bytes(d, dcfg["Hq"], dcfg["Hkv"], dcfg["D"])
+
+    sweep = {}
+    if args.only == "all":
+        d_one = si.paged_decode_inputs(dcfg["S"], dcfg["Hq"], dcfg["Hkv"], dcfg["D"], dcfg["page_size"], 16, 16,
+                                       dcfg["max_pages"], dcfg["seed"])
+        one_us, one_bytes = decode_back_to_back(d_one, 1)
+        d_256 = si.paged_decode_inputs(256, dcfg["Hq"], dcfg["Hkv"], dcfg["D"], dcfg["page_size"], dcfg["ctx_lo"],
+                                       dcfg["ctx_hi"], dcfg["max_pages"], dcfg["seed"])
+        big_us, big_bytes = decode_back_to_back(d_256, 1)
+        del d_one, d_256
+        sweep = {
+            "one_group_per_sequence": {"S": dcfg["S"], "us": round(one_us, 2), "bytes_per_call": one_bytes},
+            "s256": {"us": round(big_us, 2), "bytes_per_call": big_bytes, "gbps": round(big_bytes / big_us / 1e3, 1),
+                     "frac_of_hbm_peak": round(big_bytes / big_us / 1e3 / PEAK_HBM_GBPS, 4)},
+            "workload_beyond_fixed_gbps": round((dbytes - one_bytes) / (dec_avg_s * 1e6 - one_us) / 1e3, 1),
+        }
+
     # the step before decode: lease + append one token's K/V for every sequence of the
     # decode workload's shape, into an empty cache (pages leased every 16th call)
     S_, Hkv_, D_, ps_ = dcfg["S"], dcfg["Hkv"], dcfg["D"], dcfg["page_size"]
@@ -387,6 +427,7 @@ def main():
             "p_bytes": p_bytes, "fwd_p_store_gbps": round(p_bytes / (m_fwd_us * 1e-6) / 1e9, 1),
             "bwd_tflops": round(bwd_flops / (m_bwd_us * 1e-6) / 1e12, 3),
         },
+        "decode_sweep": sweep,
         "paged_prefill": {
             "workload": PREFILL, "new_tokens": ph["N"], "us_median": round(pre_us, 2), "flops": p_flops,
             "tflops": round(p_flops / (pre_us * 1e-6) / 1e12, 3),
