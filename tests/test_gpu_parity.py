@@ -404,6 +404,23 @@ def test_decode_split_many_sequences(dev, orc):
     assert rel_err(lse, rlse) <= TOL_DECODE
 
 
+def test_decode_shared_workspace(dev, orc):
+    """Calls of different sizes sharing one workspace that starts out as NaN: its
+    contents on entry do not matter, and each call's partials and slot records
+    overwrite whatever an earlier, larger or smaller, call left there."""
+    Hkv, G, D, ps, maxp = 4, 4, 64, 16, 64
+    nb = attn.attn_paged_decode_workspace_bytes(40, Hkv * G, Hkv, D, ps, maxp)
+    ws = torch.full((nb // 4,), float("nan"), device=dev)
+    for i, S in enumerate((40, 7, 33, 1, 40, 2)):
+        announce(f"decode shared workspace call {i} S={S}")
+        d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1, ctx_hi=1000,
+                                   max_pages=maxp, seed=900 + i)
+        o, lse = _decode(d, dev, workspace=ws)
+        ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
+        assert rel_err(o, ro) <= TOL_DECODE, (S, rel_err(o, ro))
+        assert rel_err(lse, rlse) <= TOL_DECODE
+
+
 def test_decode_matches_causal_last_row(dev):
     """Decode over a contiguous sequence equals the causal forward's last row."""
     announce("decode vs causal last row")
