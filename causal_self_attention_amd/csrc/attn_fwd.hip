@@ -8,11 +8,11 @@
 // maxima and exponential sums -- here folded into one log-sum-exp per row).
 //
 // Work decomposition (MI355X-first; the pages' tile-8 kernels are not reused):
-//   * one work-group = 8 waves = 64 query rows of one (batch, query head); wave w
-//     owns rows q0+16(w%4) .. +15 and the key half w/4 of every 64-key tile, so
-//     the heaviest (longest-prefix) blocks have half the serial work per wave;
-//     the two halves keep separate softmax statistics and are merged through
-//     LDS at the end;
+//   * one work-group = 4 x KQ waves = 64 query rows of one (batch, query head);
+//     wave w owns rows q0+16(w%4) .. +15 and key part w/4 (KQ = 2 halves, or 4
+//     quarters at d = 128) of every 64-key tile, so the heaviest (longest-prefix)
+//     blocks have a fraction of the serial work per wave; the parts keep separate
+//     softmax statistics and are merged through LDS at the end;
 //   * K/V tiles of 64 keys are staged in LDS through registers (the next tile's
 //     global loads are in flight while the current tile is multiplied);
 //   * each wave computes S^T = K Q^T on fp32 MFMA (16x16x4) with its Q rows held
@@ -34,11 +34,12 @@
 
 namespace attn {
 
-template <int D>
+template <int D, int KQ>
 struct FwdTraits {
     static constexpr int BM = 64;                     // query rows per work-group
     static constexpr int BN = 64;                     // keys per K/V tile
-    static constexpr int NT = 512;                    // threads per work-group (8 waves)
+    static constexpr int NT = 256 * KQ;               // threads per work-group: 4 row groups x KQ key parts
+    static constexpr int SUBS = 4 / KQ;               // 16-key sub-tiles of every tile per wave
     static constexpr int W = D >= 16 ? 4 : 2;         // contiguous head-dim values per lane in a fragment
     static constexpr int KSTEPS = D / 4;              // MFMA k-steps over the head dim
     static constexpr int DP = D >= 16 ? D : 16;       // head dim padded to whole 16-column O tiles
@@ -48,9 +49,10 @@ struct FwdTraits {
     static constexpr int TILE4 = BN * D / 4;          // float4 loads per K (or V) tile
     static constexpr int PER = (TILE4 + NT - 1) / NT; // float4 loads per thread per tile
     static constexpr int KS_FLOATS = BN * LDK;
-    static constexpr int SMEM_FLOATS = BN * LDK + BN * LDV;
     static constexpr int MERGE_REGS = 4 * NDT + 2;    // per lane: O accumulators, max, sum
-    static_assert(4 * MERGE_REGS * 64 <= SMEM_FLOATS, "merge buffer must fit in the K/V tiles");
+    static constexpr int MERGE_FLOATS = (KQ - 1) * 4 * MERGE_REGS * 64;  // key parts 1.. hand over
+    static constexpr int TILE_FLOATS = BN * LDK + BN * LDV;
+    static constexpr int SMEM_FLOATS = TILE_FLOATS > MERGE_FLOATS ? TILE_FLOATS : MERGE_FLOATS;
 };
 
 // Head-dim index of fragment slot s held by lane row g: groups of W contiguous
@@ -61,6 +63,14 @@ __device__ __forceinline__ constexpr int frag_dim(int s, int g) {
 }
 
 constexpr float kFwdLazyRescale = 8.f;  // log2 headroom before the running max is moved
+// key parts per tile (waves per row group).  Measured on one MI355X: at d = 128 four
+// parts (16 waves, 4 per SIMD, 114 registers) beat two (whose ~150 registers left one
+// 8-wave work-group per CU): 188.5 vs 228.2 us for B=2 H=8 T=2048; at d <= 64 two
+// parts are faster (52.6 vs 55.7 us at B=4 H=8 T=1024, 1230 vs 1328 us at the
+// 8192-token grouped-query forward), the shorter per-wave MFMA chains of four parts
+// costing more than the occupancy gains.
+template <int D>
+constexpr int fwd_key_parts() { return D >= 128 ? 4 : 2; }
 
 template <int N>
 __device__ __forceinline__ void lds_vec(const float* p, float (&x)[N]) {
@@ -80,12 +90,12 @@ __device__ __forceinline__ void lds_vec(const float* p, float (&x)[N]) {
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(512) void attn_fwd_kernel(
+template <int D, int KQ>
+__global__ __launch_bounds__(256 * KQ) void attn_fwd_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int Hq, int Hkv, int T, int nqb, int nbh, int ncu,
     float c2 /* scale * log2(e) */) {
-    using Tr = FwdTraits<D>;
+    using Tr = FwdTraits<D, KQ>;
     __shared__ __attribute__((aligned(16))) float smem[Tr::SMEM_FLOATS];
     float* Ks = smem;
     float* Vs = smem + Tr::KS_FLOATS;
@@ -94,7 +104,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
     const int lane = tid & 63;
     const int w = wave_uniform(tid >> 6);
     const int rw = w & 3;   // row group: rows q0 + 16rw .. +15
-    const int kh = w >> 2;  // key half: sub-tiles 2kh, 2kh+1 of every tile
+    const int kh = w >> 2;  // key part: sub-tiles SUBS*kh .. SUBS*kh+SUBS-1 of every tile
     const int li = lane & 15;
     const int g = lane >> 4;
 
@@ -185,12 +195,12 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
         const bool diag = (j == qb);
         const int nsub = diag ? rw + 1 : 4;  // 16-key sub-tiles with any key <= this wave's rows
 
-        // S^T = K Q^T over this wave's key half: st[tt] holds
-        // S^T[key = kv0 + 16(2kh + tt) + 4g + r][query = qrow]
-        f32x4 st[2];
+        // S^T = K Q^T over this wave's key part: st[tt] holds
+        // S^T[key = kv0 + 16(SUBS kh + tt) + 4g + r][query = qrow]
+        f32x4 st[Tr::SUBS];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * kh + tt;
+        for (int tt = 0; tt < Tr::SUBS; ++tt) {
+            const int t = Tr::SUBS * kh + tt;
             st[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (t < nsub) {
 #pragma unroll
@@ -209,11 +219,11 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
             }
         }
 
-        // mask and scale to log2 units; this lane's max over its 8 keys of the tile
+        // mask and scale to log2 units; this lane's max over its 4 SUBS keys of the tile
         float mx = -INFINITY;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * kh + tt;
+        for (int tt = 0; tt < Tr::SUBS; ++tt) {
+            const int t = Tr::SUBS * kh + tt;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int key = kv0 + 16 * t + 4 * g + r;
@@ -238,7 +248,7 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int tt = 0; tt < Tr::SUBS; ++tt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float p = exp2_hw(st[tt][r] - m_run);
@@ -250,8 +260,8 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
         // O += P V : P[query li][key 16t + 4g + r] is the A operand as it stands (k-step
         // (t, r)); B = V rows, lane li taking dims NDT*li .. NDT*li+NDT-1 as one vector
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * kh + tt;
+        for (int tt = 0; tt < Tr::SUBS; ++tt) {
+            const int t = Tr::SUBS * kh + tt;
             if (t < nsub) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -264,40 +274,55 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
         }
     }
 
-    // Merge the two key halves.  Half 1 hands its accumulators, max and sum to the
-    // half-0 wave of the same rows through LDS, in the lanes' own register layout.
-    const float l_half = rows4_sum(l_run);  // query qrow's sum over this half, in lanes (*, li)
-    float* mbuf = smem + rw * Tr::MERGE_REGS * 64 + lane;
+    // Merge the key parts.  Parts 1 .. KQ-1 hand their accumulators, max and sum to the
+    // part-0 wave of the same rows through LDS, in the lanes' own register layout.
+    const float l_part = rows4_sum(l_run);  // query qrow's sum over this part, in lanes (*, li)
     __syncthreads();  // the last tile's readers are done with the K/V buffers
-    if (kh == 1) {
+    if (kh > 0) {
+        float* mbuf = smem + ((kh - 1) * 4 + rw) * Tr::MERGE_REGS * 64 + lane;
 #pragma unroll
         for (int dt = 0; dt < Tr::NDT; ++dt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mbuf[(4 * dt + r) * 64] = acc[dt][r];
         mbuf[(4 * Tr::NDT) * 64] = m_run;
-        mbuf[(4 * Tr::NDT + 1) * 64] = l_half;
+        mbuf[(4 * Tr::NDT + 1) * 64] = l_part;
     }
     __syncthreads();
-    if (kh == 1) return;
+    if (kh > 0) return;
 
-    const float m_o = mbuf[(4 * Tr::NDT) * 64];
-    const float l_o = mbuf[(4 * Tr::NDT + 1) * 64];
-    const float m_tot = fmaxf(m_run, m_o);
-    const float a_s = exp2_hw(m_run - m_tot);  // weight of this half
-    const float a_o = exp2_hw(m_o - m_tot);    // weight of the other half
-    const float l_tot = a_s * l_half + a_o * l_o;
-    const float inv_own = 1.f / l_tot;
+    // M = max m_p, L = sum 2^(m_p - M) l_p, O = sum 2^(m_p - M) o_p / L, per query qrow
+    float m_tot = m_run;
+#pragma unroll
+    for (int p = 1; p < KQ; ++p) m_tot = fmaxf(m_tot, smem[((p - 1) * 4 + rw) * Tr::MERGE_REGS * 64 + lane + (4 * Tr::NDT) * 64]);
+    float f[KQ];  // weight of part p, then divided by L
+    float l_tot = 0.f;
+#pragma unroll
+    for (int p = 0; p < KQ; ++p) {
+        const float* mb = smem + ((p - 1) * 4 + rw) * Tr::MERGE_REGS * 64 + lane;
+        const float mp = p == 0 ? m_run : mb[(4 * Tr::NDT) * 64];
+        const float lp = p == 0 ? l_part : mb[(4 * Tr::NDT + 1) * 64];
+        f[p] = exp2_hw(mp - m_tot);
+        l_tot += f[p] * lp;
+    }
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int p = 0; p < KQ; ++p) f[p] *= inv;
     if (g == 0 && qrow < T) LSE[((size_t)b * Hq + h) * (size_t)T + qrow] = (m_tot + log2_hw(l_tot)) * kLn2;
-    const float f_s = a_s * inv_own, f_o = a_o * inv_own;
     float* Ob = O + ((size_t)b * Hq + h) * (size_t)T * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const float fs = __shfl(f_s, 4 * g + r);  // factors of query 16rw + 4g + r
-        const float fo = __shfl(f_o, 4 * g + r);
         const int q = q0 + 16 * rw + 4 * g + r;
         float out[Tr::NDT];
+        const float f0 = __shfl(f[0], 4 * g + r);  // factors of query 16rw + 4g + r
 #pragma unroll
-        for (int dt = 0; dt < Tr::NDT; ++dt) out[dt] = acc[dt][r] * fs + mbuf[(4 * dt + r) * 64] * fo;
+        for (int dt = 0; dt < Tr::NDT; ++dt) out[dt] = acc[dt][r] * f0;
+#pragma unroll
+        for (int p = 1; p < KQ; ++p) {
+            const float fp = __shfl(f[p], 4 * g + r);
+            const float* mb = smem + ((p - 1) * 4 + rw) * Tr::MERGE_REGS * 64 + lane;
+#pragma unroll
+            for (int dt = 0; dt < Tr::NDT; ++dt) out[dt] += mb[(4 * dt + r) * 64] * fp;
+        }
         if (q < T && (Tr::DP == D || li < D)) {
             float* dst = Ob + (size_t)q * D + Tr::NDT * li;
             if constexpr (Tr::NDT % 4 == 0) {
@@ -314,15 +339,17 @@ __global__ __launch_bounds__(512) void attn_fwd_kernel(
 
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
-    using Tr = FwdTraits<D>;
+    constexpr int KQ = fwd_key_parts<D>();
+    using Tr = FwdTraits<D, KQ>;
     const int nqb = (int)((a.T + Tr::BM - 1) / Tr::BM);
     const int nbh = (int)(a.B * a.Hq);
     const float c2 = a.scale * kLog2e;
     // snake order only pays when every work-group is resident at once (two per CU);
-    // for longer grids plain heaviest-first order is kept (a round as long as the grid)
+    // otherwise plain heaviest-first order (the dispatcher hands the next, lighter
+    // work-group to whichever CU frees up first)
     const int n = nqb * nbh;
-    const int ncu = n <= 2 * a.cu_count ? a.cu_count : n;
-    hipLaunchKernelGGL(attn_fwd_kernel<D>, dim3((unsigned)(nqb * nbh)), dim3(Tr::NT), 0, stream, a.q, a.k,
+    const int ncu = KQ == 2 && n <= 2 * a.cu_count ? a.cu_count : n;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, KQ>), dim3((unsigned)(nqb * nbh)), dim3(Tr::NT), 0, stream, a.q, a.k,
                        a.v, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.T, nqb, nbh, ncu, c2);
     return hipGetLastError();
 }
