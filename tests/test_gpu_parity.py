@@ -91,7 +91,8 @@ def test_gqa_t8192_forward_sampled_rows(dev, orc):
 # ---------------------------------------------------------------------------
 EDGE_CASES = [(1, 2, 2, T, D) for D in (8, 16, 32, 64, 128) for T in (1, 17, 65, 129)]
 EDGE_CASES += [(2, 3, 3, 2, 64), (1, 1, 1, 15, 32), (1, 2, 1, 63, 64), (2, 4, 2, 200, 64),
-               (1, 4, 1, 100, 64), (1, 8, 1, 77, 32), (1, 8, 2, 130, 16), (1, 16, 2, 96, 128)]
+               (1, 4, 1, 100, 64), (1, 8, 1, 77, 32), (1, 8, 2, 130, 16), (1, 16, 2, 96, 128),
+               (2, 4, 2, 777, 128)]  # d = 128: the forward's four key parts over 13 tiles
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,D", EDGE_CASES)
