@@ -24,7 +24,9 @@ mathematics fix:
 The mutation test (test_oracle_mutants.py) builds broken copies of the oracle
 and checks that each one trips at least one of these pins.
 """
+import json
 import math
+import os
 
 import numpy as np
 import torch
@@ -33,6 +35,8 @@ import synthetic_inputs as si
 
 RTOL_EXACT = 1e-12
 
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 def _rel(a, b):
     a = np.asarray(a, dtype=np.float64)
@@ -251,15 +255,19 @@ def pin_rational_example(orc):
 
 def pin_large_logits(orc):
     """The learn/neural_network page ("Stable softmax and cross-entropy") requires
-    a finite softmax for logits such as 10000, 10001, 10002; softmax is
-    shift-invariant, so that row equals softmax(0, 1, 2)."""
-    q = np.ones((1, 1, 3, 1))
-    k = np.array([10000.0, 10001.0, 10002.0]).reshape(1, 1, 3, 1)
-    _, lse, p = orc.causal_fwd(q, k, np.zeros((1, 1, 3, 1)), 1.0, return_p=True)
-    e = np.exp([0.0, 1.0, 2.0])
+    a finite softmax for the logits it prints (tests/golden/stable_softmax_large_logits.json);
+    softmax is shift-invariant, so the last row, which sees all three, equals
+    softmax(z - max z)."""
+    with open(os.path.join(GOLDEN, "stable_softmax_large_logits.json")) as f:
+        z = np.array(json.load(f)["logits"], dtype=np.float64)
+    n = z.size
+    q = np.ones((1, 1, n, 1))
+    k = z.reshape(1, 1, n, 1)
+    _, lse, p = orc.causal_fwd(q, k, np.zeros((1, 1, n, 1)), 1.0, return_p=True)
+    e = np.exp(z - z.max())
     assert np.all(np.isfinite(p)) and np.all(np.isfinite(lse))
-    assert _rel(p[0, 0, 2], e / e.sum()) < 1e-15
-    assert abs(lse[0, 0, 2] - (10002.0 + math.log(e.sum() / e[2]))) < 1e-9
+    assert _rel(p[0, 0, n - 1], e / e.sum()) < 1e-15
+    assert abs(lse[0, 0, n - 1] - (z.max() + math.log(e.sum()))) < 1e-9
 
 
 # ----------------------------------------------------------------------------
