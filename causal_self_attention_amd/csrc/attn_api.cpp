@@ -73,6 +73,13 @@ attn_status check_ptr(const void* p, const char* name, size_t align) {
 
 const int64_t kMaxElems = (int64_t)1 << 31;  // per-head T*D and index arithmetic limit
 
+// Launch grids: one forward work-group per 64-row block and head; the backward's
+// preprocess takes D/4 threads per row.  Both stay far below 2^31 work-groups here
+// (B*Hq*T*D < 2^40 floats is 4 TB, beyond any device memory).
+bool causal_grid_fits(int64_t B, int64_t Hq, int64_t T, int64_t D) {
+    return (T + 63) / 64 * (B * Hq) < kMaxElems && B * Hq * T * D < ((int64_t)1 << 40);
+}
+
 // Shape checks shared by the two causal calls.
 attn_status check_causal_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, float scale) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0)
@@ -85,6 +92,9 @@ attn_status check_causal_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, in
     if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
     if (T * D >= kMaxElems || B * Hq >= kMaxElems || T >= kMaxElems / 64)
         return fail(ATTN_INVALID_ARGUMENT, "tensor too large: T*D and B*Hq must stay below 2^31");
+    if (!causal_grid_fits(B, Hq, T, D))
+        return fail(ATTN_INVALID_ARGUMENT, "tensor too large: ceil(T/64)*B*Hq row blocks must stay below 2^31 and "
+                                           "B*Hq*T*D below 2^40");
     if (!attn::causal_head_dim_supported(D))
         return fail(ATTN_UNSUPPORTED, "head width D=" + std::to_string(D) +
                                           " has no kernel (supported: 8, 16, 32, 64, 128)");
@@ -157,7 +167,7 @@ attn_status attn_causal_fwd(const float* q, const float* k, const float* v, int6
 
 size_t attn_causal_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
-    if (T * D >= kMaxElems || B * Hq >= kMaxElems) return 0;
+    if (T * D >= kMaxElems || B * Hq >= kMaxElems || !causal_grid_fits(B, Hq, T, D)) return 0;
     const size_t bytes = attn::bwd_workspace_floats(B, Hq, T) * 4;
     return (bytes + 255) / 256 * 256;
 }

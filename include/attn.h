@@ -97,7 +97,9 @@ const char* attn_last_error(void);
  *   lse    [B, Hq,  T]      out: natural-log log-sum-exp of each score row,
  *                           m + ln(sum exp(s - m)) over the unmasked keys
  * q, k, v, o 16-byte aligned, lse 4-byte aligned; o and lse may not overlap
- * any input or each other.  T * D and B * Hq must stay below 2^31.
+ * any input or each other.  T * D, B * Hq and ceil(T / 64) * B * Hq must stay
+ * below 2^31 and B * Hq * T * D below 2^40 (ATTN_INVALID_ARGUMENT otherwise; the
+ * same limits hold for attn_causal_bwd).
  */
 attn_status attn_causal_fwd(const float* q, const float* k, const float* v,
                             int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D,

@@ -174,6 +174,10 @@ def test_fwd_invalid_arguments(L):
     _expect(_fwd(L, D=256), attn.ATTN_UNSUPPORTED, "D=256")
     _expect(_fwd(L, k=ctypes.c_void_p(0x200000008)), attn.ATTN_INVALID_ARGUMENT, "aligned")
     _expect(_fwd(L, T=1 << 30, D=64), attn.ATTN_INVALID_ARGUMENT, "too large")
+    _expect(_fwd(L, B=1 << 20, Hq=256, Hkv=256, T=4096, D=64), attn.ATTN_INVALID_ARGUMENT, "row blocks")
+    _expect(_bwd(L, B=1 << 16, Hq=256, Hkv=256, T=1 << 16, D=128, ws_bytes=1 << 40), attn.ATTN_INVALID_ARGUMENT,
+            "row blocks")
+    assert attn.attn_causal_bwd_workspace_bytes(1 << 16, 256, 256, 1 << 16, 128) == 0
     # o overlaps q; lse overlaps o
     _expect(_fwd(L, o=ctypes.c_void_p(0x100000000 + 64)), attn.ATTN_INVALID_ARGUMENT, "overlaps")
     _expect(_fwd(L, lse=ctypes.c_void_p(0x400000000 + 16)), attn.ATTN_INVALID_ARGUMENT, "overlap")
