@@ -106,8 +106,8 @@ def main():
                     help="'bwd': run only the timed steps of forward + backward (for counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "multi-GPU sharding is a design note, not an implemented path", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU (got --gpus {args.gpus}); "
+              "sharding across GPUs is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
