@@ -15,10 +15,12 @@
 //      list, are dealt out in equal contiguous shares to a grid sized to the
 //      chip, so every CU streams about the same number of bytes however ragged
 //      the context lengths are; the waves of a work-group are neighbouring KV
-//      heads of the same positions, so a page is read contiguously.  Both small
-//      contractions (scores of the G query heads that share the KV head, and the
-//      probability-weighted sum of V) run on fp32 MFMA, which is otherwise idle
-//      here; this takes the multiply-adds and their cross-lane reductions off the
+//      heads of the same positions, so a page is read contiguously.  With up to 4
+//      query heads per KV head (G / 2 flops per byte) the two small contractions
+//      (scores of the G query heads that share the KV head, and the
+//      probability-weighted sum of V) run on the vector ALU, with each lane
+//      owning a slice of the head dimension; with more they run on fp32 MFMA,
+//      which takes the multiply-adds and their cross-lane reductions off the
 //      vector ALU, whose issue rate would otherwise bound the kernel below the
 //      HBM rate.  Each K and V row is read exactly once per KV head, as
 //      contiguous vectors.  Positions past the context get score -inf and a zero
@@ -422,10 +424,10 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Split path for up to 8 query heads per KV head, on the vector ALUs.  A cached
+// Split path for up to 4 query heads per KV head, on the vector ALUs.  A cached
 // position costs 4 G D flops for 8 D bytes of K and V, i.e. G / 2 flops per byte:
-// at G <= 8 the VALU keeps up with HBM with room to spare, while a 16x16x4 MFMA
-// tile would pad the G heads to 16 columns and spend most of its cycles on zeros.
+// at G <= 4 the VALU keeps up with HBM, while a 16x16x4 MFMA tile would pad the G
+// heads to 16 columns and spend most of its cycles on zeros.
 // Layout (ND = D / 8 lanes per position, NP = 64 / ND positions per step):
 //   lane = dq + ND * pl owns head dims 4dq .. 4dq+3 and D/2 + 4dq .. D/2 + 4dq+3 of
 //   position pl of the step, so each of its two float4 loads covers ND * 16
@@ -561,7 +563,7 @@ __device__ __forceinline__ void decode_valu_span(const float* __restrict__ Kp, c
     }
 }
 
-// The split kernel for G <= GM query heads per KV head (GM = 1, 2, 4 or 8): the same
+// The split kernel for G <= GM query heads per KV head (GM = 1, 2 or 4): the same
 // partition, grid and partial slots as the MFMA split kernel above; each wave keeps
 // its copy of the per-sequence records in its own LDS area.
 template <int D, int GM, int NCH>
@@ -840,17 +842,20 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     float* Pl = Pm + (size_t)(slots * a.Hq);
     int32_t* Meta = (int32_t*)(Pl + (size_t)(slots * a.Hq));
     const int64_t G = a.Hq / a.Hkv;
-    if (G <= 8) {
-        // up to 8 query heads per KV head: the VALU split kernel, instantiated for the
-        // smallest head capacity GM >= G and the partition's chunk count
+    if (G <= 4) {
+        // up to 4 query heads per KV head: the VALU split kernel, instantiated for the
+        // smallest head capacity GM >= G and the partition's chunk count.  Measured at
+        // 32 sequences it beats the MFMA kernel for G = 1..4 (57.4 vs 68.2 us at G = 4,
+        // d = 128; 94.1 vs 100.1 us at G = 1, d = 64; 5 % behind at d = 32) and loses
+        // for G = 6..8 (44.7 vs 33.7 us at G = 8, d = 64), where the VALU work per byte
+        // has doubled and the MFMA tile is at most half padding.
         const bool one = a.S <= 64;
         const int nch = one ? 1 : kDecodeScanChunks;
         auto pick = [&](auto k1, auto k16) { return one ? k1 : k16; };
         decltype(&attn_decode_split_valu_kernel<D, 1, 1>) valu =
             G == 1   ? pick(attn_decode_split_valu_kernel<D, 1, 1>, attn_decode_split_valu_kernel<D, 1, kDecodeScanChunks>)
             : G == 2 ? pick(attn_decode_split_valu_kernel<D, 2, 1>, attn_decode_split_valu_kernel<D, 2, kDecodeScanChunks>)
-            : G <= 4 ? pick(attn_decode_split_valu_kernel<D, 4, 1>, attn_decode_split_valu_kernel<D, 4, kDecodeScanChunks>)
-                     : pick(attn_decode_split_valu_kernel<D, 8, 1>, attn_decode_split_valu_kernel<D, 8, kDecodeScanChunks>);
+                     : pick(attn_decode_split_valu_kernel<D, 4, 1>, attn_decode_split_valu_kernel<D, 4, kDecodeScanChunks>);
         const size_t lds = (size_t)wpw * 64 * nch * sizeof(int4);
         hipLaunchKernelGGL(valu, dim3((unsigned)nwg, (unsigned)gy), dim3(64 * wpw), lds, stream, a.q, a.k_pool,
                            a.v_pool, a.block_table, a.context_lens, Po, Pm, Pl, Meta, (int)a.S, (int)a.Hq,
