@@ -168,7 +168,7 @@ attn_status attn_causal_fwd(const float* q, const float* k, const float* v, int6
 size_t attn_causal_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || Hq % Hkv != 0) return 0;
     if (T * D >= kMaxElems || B * Hq >= kMaxElems || !causal_grid_fits(B, Hq, T, D)) return 0;
-    const size_t bytes = attn::bwd_workspace_floats(B, Hq, T) * 4;
+    const size_t bytes = attn::bwd_workspace_floats(B, Hq, Hkv, T, D) * 4;
     return (bytes + 255) / 256 * 256;
 }
 

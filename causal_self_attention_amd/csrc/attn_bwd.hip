@@ -21,9 +21,15 @@
 //      For a short grid the heaviest key block alone would set the kernel's
 //      length (key block 0 has the most steps), so the key blocks are ordered
 //      0, n-1, 1, n-2, ... -- every such pair has the same number of steps -- and
-//      each work-group takes half a pair.  A key block that is cut in two adds
-//      its dK, dV atomically onto zero; two addends onto zero give the same bits
-//      in either order, so the result stays deterministic.  Within a key block,
+//      the list is cut into equal runs, one per work-group: half a pair each, or,
+//      when that leaves CUs idle (few batch x KV heads, e.g. grouped-query heads
+//      at small batch), as many runs as the chip holds work-groups.  With half
+//      pairs a key block that is cut in two adds its dK, dV atomically onto
+//      zero; two addends onto zero give the same bits in either order.  With
+//      finer runs a block can be cut into more pieces: each run then stores its
+//      piece in a workspace slot of its own, and
+//   3. attn_bwd_post sums the pieces of each shared block in run order.  Either
+//      way dK, dV are deterministic.  Within a key block,
 //      wave w owns keys kv0+16w .. +15 and keeps their K, V fragments and dK, dV
 //      accumulators in registers.  Per step (64 query rows, Q and dO in LDS):
 //        S  = Q K^T, dP = dO V^T           (C tiles: key in the lane i)
@@ -33,6 +39,8 @@
 //                                           lane i owns dims NDT*i .. NDT*i+NDT-1)
 //        dS -> LDS, then dQ(16 rows per wave) = dS K, added to dQ with float
 //        atomics (the contraction runs over the whole 64-key block).
+#include <algorithm>
+
 #include "attn_launch.h"
 #include "device_common.h"
 
@@ -125,8 +133,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     const float* __restrict__ P, const float* __restrict__ dPx,
-    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
-    int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV,
+    float* __restrict__ part /* finer runs: per run, two pieces of dK, dV [BN, D] each; else NULL */,
+    int Hq, int Hkv, int T, int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         const int pr = pi >> 1;
         return pr * pair_len + ((pi & 1) ? (int64_t)G * (nkb - pr) : 0);
     };
-    int bkv, pi = 0, kb_fixed = 0;
+    int bkv, pi = 0, kb_fixed = 0, run = 0;
     int64_t s_begin, s_end;
     if (runs == 0) {  // one work-group per key block, heaviest first
         const int rank = blockIdx.x;
@@ -161,8 +170,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         bkv = rank % nbkv;
         s_begin = 0;
         s_end = (int64_t)G * (nqb - kb_fixed);
-    } else {  // run `run` of `runs` (== nkb) equal runs: half a pair each
-        const int run = blockIdx.x / nbkv;
+    } else {  // run `run` of `runs` equal runs (runs == nkb: half a pair each)
+        run = blockIdx.x / nbkv;
         bkv = blockIdx.x % nbkv;
         const int64_t total = (int64_t)G * nkb * (nkb + 1) / 2;
         s_begin = (int64_t)run * total / runs;
@@ -199,6 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         const int64_t kb_end = kb_first + (int64_t)G * (nqb - kb);
         const int64_t seg_end = s_end < kb_end ? s_end : kb_end;
         const bool whole = (s == kb_first && seg_end == kb_end);  // no other run shares this key block
+        const bool first_seg = (s == s_begin);  // a shared block is a run's first or its last segment
         const int j0 = (int)(s - kb_first), j1 = (int)(seg_end - kb_first);
         s = seg_end;
         const int nqt = nqb - kb;
@@ -450,13 +460,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         }
 
         // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1.
-        if (whole) {  // no other run shares this key block: plain stores
+        if (whole || part) {
+            // plain stores: into dK, dV when no other run shares this key block, else
+            // into this run's slot for its first (0) or last (1) segment
+            float* dKb = dKh + (size_t)kv0 * D;
+            float* dVb = dVh + (size_t)kv0 * D;
+            if (!whole) {
+                dKb = part + (((size_t)bkv * runs + run) * 2 + (first_seg ? 0 : 1)) * (2 * Tr::BN * D);
+                dVb = dKb + Tr::BN * D;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = kv0 + 16 * w + 4 * g + r;
-                if (key < T && (Tr::DP == D || li < D)) {
-                    float* dKr = dKh + (size_t)key * D + Tr::NDT * li;
-                    float* dVr = dVh + (size_t)key * D + Tr::NDT * li;
+                const int row = 16 * w + 4 * g + r;
+                if (kv0 + row < T && (Tr::DP == D || li < D)) {
+                    float* dKr = dKb + (size_t)row * D + Tr::NDT * li;
+                    float* dVr = dVb + (size_t)row * D + Tr::NDT * li;
                     if constexpr (Tr::NDT % 4 == 0) {
 #pragma unroll
                         for (int dt = 0; dt < Tr::NDT; dt += 4) {
@@ -498,19 +516,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     }
 }
 
+// ---------------------------------------------------------------------------
+// 3. finer runs only: dK, dV of the key blocks that several runs share
+// ---------------------------------------------------------------------------
+// One work-group per (256 float4 of a key block's dK, dV; key block; batch x KV
+// head).  The runs that hold a piece of the block are found from the same equal cut
+// of the step list as in the main kernel, and their pieces are summed in run order,
+// so the bits do not depend on which run finished first.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_post_kernel(const float* __restrict__ part, float* __restrict__ dK,
+                                                            float* __restrict__ dV, int G, int T, int nkb, int nbkv,
+                                                            int runs) {
+    constexpr int BN = BwdTraits<D>::BN;
+    constexpr int ROW4 = D / 4;  // float4 per key row
+    const int blk = blockIdx.x % (nbkv * nkb);
+    const int idx = (blockIdx.x / (nbkv * nkb)) * 256 + threadIdx.x;  // float4 of [dK; dV] of the block
+    const int bkv = blk % nbkv;
+    const int kb = blk / nbkv;
+    // the block's place in the paired order 0, nkb-1, 1, nkb-2, ... and its step range
+    const int pi = 2 * kb < nkb ? 2 * kb : 2 * (nkb - 1 - kb) + 1;
+    const int pr = pi >> 1;
+    const int64_t pair_len = (int64_t)G * (nkb + 1);
+    const int64_t bs = pr * pair_len + ((pi & 1) ? (int64_t)G * (nkb - pr) : 0);
+    const int64_t be = bs + (int64_t)G * (nkb - kb);
+    const int64_t total = (int64_t)G * nkb * (nkb + 1) / 2;
+    // run r holds steps [r * total / runs, (r + 1) * total / runs)
+    const int r0 = (int)(((bs + 1) * runs - 1) / total);
+    const int r1 = (int)((be * runs - 1) / total);
+    if (r0 == r1) return;  // a single run held the block and stored it
+    if (idx >= 2 * BN * ROW4) return;
+    const int half = idx / (BN * ROW4);  // 0: dK, 1: dV
+    const int e = idx % (BN * ROW4);
+    const int key = kb * BN + e / ROW4;
+    if (key >= T) return;
+    // the block is run r0's first segment if r0 starts on it, else r0's last; it is
+    // the first segment of every later run that holds a piece of it
+    const int w0 = (int64_t)r0 * total / runs == bs ? 0 : 1;
+    constexpr size_t PIECE = 2 * (size_t)BN * D;  // dK then dV, [BN, D] each
+    const float* base = part + (size_t)bkv * runs * 2 * PIECE + (size_t)half * BN * D + 4 * (size_t)e;
+    f32x4 acc = *(const f32x4*)(base + ((size_t)r0 * 2 + w0) * PIECE);
+    int r = r0 + 1;
+    for (; r + 4 <= r1 + 1; r += 4) {  // four loads in flight, added in run order
+        const f32x4 x0 = *(const f32x4*)(base + (size_t)r * 2 * PIECE);
+        const f32x4 x1 = *(const f32x4*)(base + (size_t)(r + 1) * 2 * PIECE);
+        const f32x4 x2 = *(const f32x4*)(base + (size_t)(r + 2) * 2 * PIECE);
+        const f32x4 x3 = *(const f32x4*)(base + (size_t)(r + 3) * 2 * PIECE);
+        acc += x0;
+        acc += x1;
+        acc += x2;
+        acc += x3;
+    }
+    for (; r <= r1; ++r) acc += *(const f32x4*)(base + (size_t)r * 2 * PIECE);
+    *(f32x4*)((half ? dV : dK) + ((size_t)bkv * T + key) * D + 4 * (e % ROW4)) = acc;
+}
+
+// Runs per (batch, KV head) of the finer cut at most: the total over the grid stays
+// within kBwdMaxRunWgs and every run gets at least two steps; 0 when this is no
+// finer than half pairs.
+static int64_t bwd_fine_runs_max(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) {
+    const int64_t nkb = (T + 63) / 64, nbkv = B * Hkv;
+    const int64_t total = Hq / Hkv * nkb * (nkb + 1) / 2;
+    const int64_t r = std::min<int64_t>(kBwdMaxRunWgs / nbkv, total / 2);
+    return r > nkb ? r : 0;
+}
+
+static size_t bwd_delta_floats(int64_t B, int64_t Hq, int64_t T) { return (size_t)(B * Hq * T + 63) / 64 * 64; }
+
 template <int D, bool MAT>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     using Tr = BwdTraits<D>;
+    static_assert(Tr::BN == 64, "bwd_fine_runs_max counts 64-key blocks");
     const int nkb = (int)((a.T + Tr::BN - 1) / Tr::BN);
     const int nbkv = (int)(a.B * a.Hkv);
     const int n = nkb * nbkv;  // work-groups with one key block each
-    // Two work-groups fit on a CU.  When all key blocks are resident at once, the
-    // heaviest one alone would set the kernel's length: take half pairs instead.
-    const int runs = n <= 2 * a.cu_count ? nkb : 0;
+    // Two work-groups fit on a CU (one at D >= 128).  When all key blocks are
+    // resident at once, the heaviest one alone would set the kernel's length: take
+    // half pairs instead, or finer runs when half pairs leave CUs without work.
+    int runs = 0;
+    float* part = nullptr;
+    if (n <= 2 * a.cu_count) {
+        runs = nkb;
+        const int64_t slots = (int64_t)(D >= 128 ? 1 : 2) * a.cu_count;
+        const int64_t fine = std::min<int64_t>(slots / nbkv, bwd_fine_runs_max(a.B, a.Hq, a.Hkv, a.T));
+        if (fine > nkb) {
+            runs = (int)fine;
+            part = a.delta + bwd_delta_floats(a.B, a.Hq, a.T);
+        }
+    }
     const int64_t rows = a.B * a.Hq * a.T;
-    // Only the first key block of a pair can be cut in two (the cut falls inside
-    // it), so only key blocks 0 .. nkb/2 - 1 are added atomically and need zeroing.
-    int64_t zrows = runs > 0 ? (int64_t)(nkb / 2) * Tr::BN : 0;
+    // With half pairs only the first key block of a pair can be cut in two (the cut
+    // falls inside it), so only key blocks 0 .. nkb/2 - 1 are added atomically and
+    // need zeroing.  Finer runs store every block.
+    int64_t zrows = runs > 0 && !part ? (int64_t)(nkb / 2) * Tr::BN : 0;
     if (zrows > a.T) zrows = a.T;
     constexpr int RPB = 256 / (D / 4);
     const int64_t pre_blocks = (rows + RPB - 1) / RPB + (nbkv * zrows + RPB - 1) / RPB;
@@ -524,12 +621,21 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     }
     const unsigned grid = runs > 0 ? (unsigned)(runs * nbkv) : (unsigned)n;
     hipLaunchKernelGGL((attn_bwd_main_kernel<D, MAT>), dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v,
-                       a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
-                       nbkv, runs, a.scale, a.scale * kLog2e);
+                       a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, part, (int)a.Hq, (int)a.Hkv, (int)a.T,
+                       nkb, nbkv, runs, a.scale, a.scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess || !part) return e;
+    constexpr int chunks = (2 * Tr::BN * D / 4 + 255) / 256;
+    hipLaunchKernelGGL(attn_bwd_post_kernel<D>, dim3((unsigned)(n * chunks)), dim3(256), 0, stream, part, a.dk,
+                       a.dv, (int)(a.Hq / a.Hkv), (int)a.T, nkb, nbkv, runs);
     return hipGetLastError();
 }
 
-size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t T) { return (size_t)(B * Hq * T); }
+size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D) {
+    // Delta [B, Hq, T], then, when the grid may be cut finer than half pairs, two
+    // pieces of dK, dV per run
+    return bwd_delta_floats(B, Hq, T) + (size_t)(B * Hkv) * bwd_fine_runs_max(B, Hq, Hkv, T) * 2 * 2 * 64 * D;
+}
 
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream) {
     switch (a.D) {

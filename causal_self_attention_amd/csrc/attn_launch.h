@@ -21,7 +21,7 @@ struct FwdArgs {
 struct BwdArgs {
     const float *q, *k, *v, *o, *lse, *dout;
     float *dq, *dk, *dv;
-    float* delta;  // workspace: [B, Hq, T]
+    float* delta;  // workspace: Delta [B, Hq, T], then the finer cut's dK, dV pieces
     int64_t B, Hq, Hkv, T, D;
     float scale;
     int cu_count;
@@ -93,7 +93,10 @@ bool causal_head_dim_supported(int64_t D);
 bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group);
 
 // Workspace sizes in floats.
-size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t T);
+size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D);
+// Work-groups of the backward's finer cut at most (two per CU of a 256-CU chip; it
+// bounds that cut's workspace)
+constexpr int64_t kBwdMaxRunWgs = 512;
 size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages);
 

@@ -106,7 +106,9 @@ attn_status attn_causal_fwd(const float* q, const float* k, const float* v,
                             float scale, float* o, float* lse, void* stream);
 
 /* Bytes of device workspace attn_causal_bwd needs for these sizes (0 when a
- * size is invalid). */
+ * size is invalid): one float per query row, and, when B * Hkv * ceil(T / 64)
+ * is small enough that the work is cut finer than per key block (at most 512
+ * pieces of work), two 64 x D slices of dK and of dV per piece. */
 size_t attn_causal_bwd_workspace_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D);
 
 /*

@@ -63,7 +63,17 @@ def test_version_and_status_values(L):
 
 
 def test_workspace_queries(L):
-    assert attn.attn_causal_bwd_workspace_bytes(4, 8, 8, 1024, 64) == 4 * 8 * 1024 * 4
+    def bwd_expect(B, Hq, Hkv, T, D):
+        # Delta (rounded to 64 floats), then two dK, dV pieces [64, D] per run of the
+        # finer cut (at most 512 work-groups, two steps each, only if finer than T/64)
+        nkb = (T + 63) // 64
+        fine = min(512 // (B * Hkv), Hq // Hkv * nkb * (nkb + 1) // 2 // 2)
+        fine = fine if fine > nkb else 0
+        floats = (B * Hq * T + 63) // 64 * 64 + B * Hkv * fine * 2 * 2 * 64 * D
+        return (floats * 4 + 255) // 256 * 256
+    assert attn.attn_causal_bwd_workspace_bytes(4, 8, 8, 1024, 64) == 4 * 8 * 1024 * 4  # no finer cut
+    for args in ((4, 8, 2, 1024, 64), (1, 8, 8, 2048, 128), (1, 2, 2, 16, 8), (2, 4, 1, 200, 32), (1, 1, 1, 64, 8)):
+        assert attn.attn_causal_bwd_workspace_bytes(*args) == bwd_expect(*args), args
     assert attn.attn_causal_bwd_workspace_bytes(1, 2, 2, 16, 8) == 256  # rounded up to 256
     assert attn.attn_causal_bwd_workspace_bytes(1, 3, 2, 16, 8) == 0    # Hq % Hkv != 0
     assert attn.attn_causal_bwd_workspace_bytes(0, 2, 2, 16, 8) == 0

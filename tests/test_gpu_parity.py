@@ -146,11 +146,48 @@ def test_backward_whole_key_block_schedule(dev, orc, Hq, Hkv, D):
     _check_fwd_bwd(dev, orc, B, Hq, Hkv, T, D, seed=300 + D)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(1, 8, 2, 777, 32), (1, 1, 1, 1088, 64), (3, 6, 3, 960, 16)])
-def test_backward_half_pair_schedule(dev, orc, B, Hq, Hkv, T, D):
-    """Few key blocks: half pairs of key blocks per work-group, odd and even counts."""
-    announce(f"bwd half-pair schedule B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
-    _check_fwd_bwd(dev, orc, B, Hq, Hkv, T, D, seed=400 + T)
+def _bwd_schedule(cus, B, Hq, Hkv, T, D):
+    """Which cut of the backward's work the library takes for this shape on `cus` CUs:
+    one whole key block per work-group, half pairs of key blocks, or finer runs (as
+    many as the chip holds work-groups, at most 512, at least two steps each)."""
+    nkb, nbkv = (T + 63) // 64, B * Hkv
+    if nkb * nbkv > 2 * cus:
+        return "whole"
+    fine = min((1 if D >= 128 else 2) * cus // nbkv, 512 // nbkv, Hq // Hkv * nkb * (nkb + 1) // 2 // 2)
+    return "fine" if fine > nkb else "half"
+
+
+@pytest.mark.parametrize("nbkv,Hkv,G,D", [(32, 8, 1, 64), (39, 13, 1, 32), (16, 8, 1, 128), (22, 2, 3, 16)])
+def test_backward_half_pair_schedule(dev, orc, nbkv, Hkv, G, D):
+    """Key blocks that just fill the chip: half pairs of key blocks per work-group, odd and
+    even counts of blocks, the last one ragged."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    B = nbkv // Hkv
+    nkb = (1 if D >= 128 else 2) * cus // nbkv
+    T = 64 * nkb - 23
+    assert _bwd_schedule(cus, B, G * Hkv, Hkv, T, D) == "half"
+    announce(f"bwd half-pair schedule B={B} Hq={G * Hkv} Hkv={Hkv} T={T} D={D}")
+    _check_fwd_bwd(dev, orc, B, G * Hkv, Hkv, T, D, seed=400 + T)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,D", [(1, 8, 2, 777, 32), (1, 1, 1, 1088, 64), (3, 6, 3, 960, 16),
+                                          (1, 8, 1, 512, 64), (2, 8, 2, 1000, 128)])
+def test_backward_fine_schedule(dev, orc, B, Hq, Hkv, T, D):
+    """Few batch x KV heads: the step list cut into as many runs as the chip holds, so a key
+    block is shared by many runs (up to 32 at B=1, Hkv=1, T=512), whose pieces are summed in
+    run order: parity, and bitwise equal dK, dV on a second call."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert _bwd_schedule(cus, B, Hq, Hkv, T, D) == "fine"
+    announce(f"bwd fine schedule B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    host = si.causal_inputs(B, Hq, Hkv, T, D, seed=450 + T + D)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    dq, dk, dv = _run_bwd(x, o, lse)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+    _, dk2, dv2 = _run_bwd(x, o, lse)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
 # ---------------------------------------------------------------------------
