@@ -171,8 +171,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         s_begin = 0;
         s_end = (int64_t)G * (nqb - kb_fixed);
     } else {  // run `run` of `runs` equal runs (runs == nkb: half a pair each)
-        run = blockIdx.x / nbkv;
-        bkv = blockIdx.x % nbkv;
+        // Runs alternate between the floor and the ceiling of total / runs steps.  When
+        // the grid fills the chip once, work-groups i and i + grid/2 share a CU: give
+        // them neighbouring runs, so every CU carries the same number of steps.
+        const int half_grid = (int)(gridDim.x / 2);
+        if ((runs & 1) == 0) {
+            const int hi = (int)blockIdx.x >= half_grid ? 1 : 0;
+            const int j = (int)blockIdx.x - hi * half_grid;
+            run = 2 * (j / nbkv) + hi;
+            bkv = j % nbkv;
+        } else {
+            run = blockIdx.x / nbkv;
+            bkv = blockIdx.x % nbkv;
+        }
         const int64_t total = (int64_t)G * nkb * (nkb + 1) / 2;
         s_begin = (int64_t)run * total / runs;
         s_end = (int64_t)(run + 1) * total / runs;
