@@ -23,9 +23,12 @@
 //   * the query rows start at an arbitrary position, so the causal mask is applied
 //     per element on every tile that reaches past a wave's first row, and 16-key
 //     sub-tiles wholly past a wave's last row are skipped;
-//   * the grid enumerates (query block, head) over the ragged batch: each work-group
-//     finds its sequence from a prefix sum of the per-sequence block counts (one
-//     wave, DPP scan), heaviest blocks (latest positions) first within a sequence.
+//   * the grid enumerates (query block, head) over the ragged batch, heaviest block
+//     (most key tiles) first over the whole batch: each work-group finds its block by
+//     bisection on the number of blocks with at least t tiles (one wave, one lane
+//     per sequence, DPP scans), so the longest blocks of every sequence start in the
+//     first round (in sequence order, the last sequence's longest blocks started
+//     last and set the kernel's end).
 #include "attn_launch.h"
 #include "device_common.h"
 
@@ -115,25 +118,79 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const int item = blockIdx.x / Hq;
     const int h = blockIdx.x % Hq;
 
-    // Which (sequence, block) is item number `item`: sequence s has ceil(n_s / 64)
-    // blocks; wave 0 scans the counts 64 sequences at a time.  Token offsets are
-    // clamped into [0, N], so a broken table gives wrong numbers, never a bad read.
+    // Which (sequence, block) is item number `item`.  Items run heaviest block first
+    // over the whole batch (most key tiles; ties by sequence, then block), so the
+    // longest blocks start in the first round and no long block is left for the end.
+    // Block qb of sequence s reaches position L = min(base + min(64qb + 64, n) - 1,
+    // ctx - 1) and visits max(L, 0) / 64 + 1 key tiles, non-decreasing in qb; the
+    // item-th largest count is found by bisection on the number of blocks with at
+    // least t tiles, which has a closed form per sequence (one lane each, 64
+    // sequences at a time).  Token offsets and lengths are clamped as below, so a
+    // broken table gives wrong numbers, never a bad read.
     if (w == 0) {
-        int carry = 0, s_sel = -1, qb_sel = 0;
-        for (int c0 = 0; c0 < S && s_sel < 0; c0 += 64) {
-            const int s = c0 + lane;
-            const int a = min(max(TS[min(s, S)], 0), N), b = min(max(TS[min(s + 1, S)], 0), N);
-            const int cnt = s < S ? (max(b - a, 0) + Tr::BM - 1) / Tr::BM : 0;
-            const int incl = carry + pf_wave_incl_scan(cnt);
-            const uint64_t hit = __ballot(item < incl);
-            if (hit) {
-                const int l = __builtin_ctzll(hit);
-                s_sel = c0 + l;
-                const int first = __builtin_amdgcn_readlane(incl - cnt, l);
-                const int n_blk = __builtin_amdgcn_readlane(cnt, l);
-                qb_sel = n_blk - 1 - (item - first);  // latest block first
+        const int cap = PS * max_pages;
+        struct SeqBlocks {
+            int nb, n, base, ctxm1;
+        };
+        auto seq_at = [&](int sq) {
+            SeqBlocks r{0, 0, 0, -1};
+            if (sq < S) {
+                const int a = min(max(TS[sq], 0), N), b = min(max(TS[sq + 1], 0), N);
+                const int n = max(b - a, 0);
+                const int ctx = min(max(CTX[sq], 0), cap);
+                r = SeqBlocks{(n + Tr::BM - 1) / Tr::BM, n, max(ctx - n, 0), ctx - 1};
             }
-            carry = __builtin_amdgcn_readlane(incl, 63);
+            return r;
+        };
+        // blocks of one sequence with at least t key tiles
+        auto cnt_ge = [&](const SeqBlocks& q, int t) {
+            if (t <= 1) return q.nb;
+            const int P = Tr::BN * (t - 1);  // L >= P  <=>  at least t tiles
+            const int R = P - q.base + 1;    // ... <=>  min(64qb + 64, n) >= R and ctx - 1 >= P
+            if (q.nb == 0 || q.ctxm1 < P || q.n < R) return 0;
+            return q.nb - (R <= Tr::BM ? 0 : (R - 1) / Tr::BM);  // first such qb: 64qb + 64 >= R
+        };
+        const SeqBlocks q0 = seq_at(lane);
+        auto total_ge = [&](int t) {
+            int tot = 0;
+            for (int c0 = 0; c0 < S; c0 += 64) {
+                const SeqBlocks q = c0 == 0 ? q0 : seq_at(c0 + lane);
+                tot += __builtin_amdgcn_readlane(pf_wave_incl_scan(cnt_ge(q, t)), 63);
+            }
+            return tot;
+        };
+        int s_sel = -1, qb_sel = 0;
+        if (item < total_ge(1)) {
+            int tmax = 0;  // most tiles of any block: the last block of some sequence
+            for (int c0 = 0; c0 < S; c0 += 64) {
+                const SeqBlocks q = c0 == 0 ? q0 : seq_at(c0 + lane);
+                const int last = q.nb > 0 ? max(min(q.base + q.n - 1, q.ctxm1), 0) / Tr::BN + 1 : 0;
+                tmax = max(tmax, last);
+            }
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) tmax = max(tmax, __shfl_xor(tmax, m));
+            int lo = 1, hi = tmax;  // total_ge(lo) > item throughout
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (total_ge(mid) > item) lo = mid;
+                else hi = mid - 1;
+            }
+            const int k = item - (lo < tmax ? total_ge(lo + 1) : 0);  // rank among blocks of lo tiles
+            int carry = 0;
+            for (int c0 = 0; c0 < S && s_sel < 0; c0 += 64) {
+                const SeqBlocks q = c0 == 0 ? q0 : seq_at(c0 + lane);
+                const int ge = cnt_ge(q, lo);
+                const int eq = ge - cnt_ge(q, lo + 1);
+                const int incl = carry + pf_wave_incl_scan(eq);
+                const uint64_t hit = __ballot(k < incl);
+                if (hit) {
+                    const int l = __builtin_ctzll(hit);
+                    s_sel = c0 + l;
+                    const int first = __builtin_amdgcn_readlane(incl - eq, l);
+                    qb_sel = __builtin_amdgcn_readlane(q.nb - ge, l) + (k - first);
+                }
+                carry = __builtin_amdgcn_readlane(incl, 63);
+            }
         }
         if (lane == 0) {
             sel[0] = s_sel;
