@@ -133,9 +133,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     const float* __restrict__ P, const float* __restrict__ dPx,
-    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV,
-    float* __restrict__ part /* finer runs: per run, two pieces of dK, dV [BN, D] each; else NULL */,
-    int Hq, int Hkv, int T, int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
+    float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
+    int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
@@ -162,7 +161,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         const int pr = pi >> 1;
         return pr * pair_len + ((pi & 1) ? (int64_t)G * (nkb - pr) : 0);
     };
-    int bkv, pi = 0, kb_fixed = 0, run = 0;
+    // Finer runs only: (bkv * runs + run) << 16 | the run's first position pi, all the
+    // epilogue needs to find a shared block's workspace slot (one register through the
+    // step loop; bkv * runs + run < 512 and pi < 2 nkb <= 1024 there).
+    int fine_tag = 0;
+    int bkv, pi = 0, kb_fixed = 0;
     int64_t s_begin, s_end;
     if (runs == 0) {  // one work-group per key block, heaviest first
         const int rank = blockIdx.x;
@@ -176,6 +179,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         // grid fills the chip once, work-groups i and i + grid/2 share a CU, and the one
         // placed first gets ahead at the start (its partner's first step took 18 us vs
         // 11 us): give the pair neighbouring runs, the longer one to work-group i.
+        int run;
         const int half_grid = (int)(gridDim.x / 2);
         if ((runs & 1) == 0) {
             const int hi = (int)blockIdx.x >= half_grid ? 1 : 0;
@@ -191,6 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         s_end = (int64_t)(run + 1) * total / runs;
         const int pr = (int)(s_begin / pair_len);
         pi = 2 * pr + (s_begin - pr * pair_len >= (int64_t)G * (nkb - pr) ? 1 : 0);
+        fine_tag = ((bkv * runs + run) << 16) | pi;
     }
     const int b = bkv / Hkv;
     const int hk = bkv % Hkv;
@@ -221,7 +226,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         const int64_t kb_end = kb_first + (int64_t)G * (nqb - kb);
         const int64_t seg_end = s_end < kb_end ? s_end : kb_end;
         const bool whole = (s == kb_first && seg_end == kb_end);  // no other run shares this key block
-        const bool first_seg = (s == s_begin);  // a shared block is a run's first or its last segment
         const int j0 = (int)(s - kb_first), j1 = (int)(seg_end - kb_first);
         s = seg_end;
         const int nqt = nqb - kb;
@@ -473,13 +477,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         }
 
         // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1.
-        if (whole || part) {
+        if (whole || runs > nkb) {
             // plain stores: into dK, dV when no other run shares this key block, else
-            // into this run's slot for its first (0) or last (1) segment
+            // (finer runs) into this run's workspace slot after Delta: slot 0 for the
+            // run's first segment, 1 for its last.
             float* dKb = dKh + (size_t)kv0 * D;
             float* dVb = dVh + (size_t)kv0 * D;
             if (!whole) {
-                dKb = part + (((size_t)bkv * runs + run) * 2 + (first_seg ? 0 : 1)) * (2 * Tr::BN * D);
+                const size_t slot = (size_t)(fine_tag >> 16) * 2 + (pi != (fine_tag & 0xFFFF) ? 1 : 0);
+                float* part = const_cast<float*>(Delta) + ((size_t)nbkv * G * T + 63) / 64 * 64;
+                dKb = part + slot * (2 * Tr::BN * D);
                 dVb = dKb + Tr::BN * D;
             }
 #pragma unroll
@@ -634,8 +641,8 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     }
     const unsigned grid = runs > 0 ? (unsigned)(runs * nbkv) : (unsigned)n;
     hipLaunchKernelGGL((attn_bwd_main_kernel<D, MAT>), dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v,
-                       a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, part, (int)a.Hq, (int)a.Hkv, (int)a.T,
-                       nkb, nbkv, runs, a.scale, a.scale * kLog2e);
+                       a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
+                       nbkv, runs, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess || !part) return e;
     constexpr int chunks = (2 * Tr::BN * D / 4 + 255) / 256;
