@@ -416,21 +416,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 // dV += P^T dO and dK += dS^T Q with P, dS as the A operands straight from their
                 // accumulators (k-step (qs, r) pairs lane row g with query 16qs + 4g + r) and the
                 // dO / Q rows as B operands, lane li taking dims NDT*li .. NDT*li+NDT-1
+                {
+                    // batches k = (qs, r), their dO and Q row slices read one batch ahead
+                    auto roff = [&](int k) { return (16 * (k / 4) + 4 * g + k % 4) * Tr::LD + Tr::NDT * li; };
+                    float bon[Tr::NDT], bqn[Tr::NDT];
+                    lds_row<Tr::NDT>(&dOs[roff(0)], bon);
+                    lds_row<Tr::NDT>(&Qs[roff(0)], bqn);
 #pragma unroll
-                for (int qs = 0; qs < 4; ++qs) {
-                    {
+                    for (int k = 0; k < 16; ++k) {
+                        float bo[Tr::NDT], bq[Tr::NDT];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int row = (16 * qs + 4 * g + r) * Tr::LD + Tr::NDT * li;
-                            float bo[Tr::NDT], bq[Tr::NDT];
-                            lds_row<Tr::NDT>(&dOs[row], bo);
-                            lds_row<Tr::NDT>(&Qs[row], bq);
-#pragma unroll
-                            for (int dt = 0; dt < Tr::NDT; ++dt) {
-                                dv[dt] = mfma16x16x4(sa[qs][r], bo[dt], dv[dt]);
-                                dk[dt] = mfma16x16x4(pa[qs][r], bq[dt], dk[dt]);
-                            }
+                        for (int dt = 0; dt < Tr::NDT; ++dt) {
+                            bo[dt] = bon[dt];
+                            bq[dt] = bqn[dt];
                         }
+                        if (k + 1 < 16) {
+                            lds_row<Tr::NDT>(&dOs[roff(k + 1)], bon);
+                            lds_row<Tr::NDT>(&Qs[roff(k + 1)], bqn);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        const int qs = k / 4, r = k % 4;
+#pragma unroll
+                        for (int dt = 0; dt < Tr::NDT; ++dt) {
+                            dv[dt] = mfma16x16x4(sa[qs][r], bo[dt], dv[dt]);
+                            dk[dt] = mfma16x16x4(pa[qs][r], bq[dt], dk[dt]);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
 
