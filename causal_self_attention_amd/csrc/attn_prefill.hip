@@ -50,7 +50,8 @@ struct PrefillTraits {
     static constexpr int TILE4 = BN * D / 4;           // float4 loads per K (or V) tile
     static constexpr int PER = (TILE4 + NT - 1) / NT;  // float4 loads per thread per tile
     static constexpr int KS_FLOATS = BN * LDK;
-    static constexpr int SMEM_FLOATS = BN * LDK + BN * LDV;
+    static constexpr int TILE_FLOATS = BN * LDK + BN * LDV;
+    static constexpr int SMEM_FLOATS = 2 * TILE_FLOATS;  // two K/V buffers
     static constexpr int MERGE_REGS = 4 * NDT + 2;     // per lane: O accumulators, max, sum
     static_assert(4 * MERGE_REGS * 64 <= SMEM_FLOATS, "merge buffer must fit in the K/V tiles");
 };
@@ -216,10 +217,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const int wave_last = min(base + min(j0 + 16 * rw + 15, n_s - 1), ctx - 1);  // this wave's last
     const int ntiles = last_pos / Tr::BN + 1;
 
-    if constexpr (Tr::DP != D) {  // zero the padding columns of V once
+    if constexpr (Tr::DP != D) {  // zero the padding columns of both V buffers once
         for (int idx = tid; idx < Tr::BN * (Tr::DP - D); idx += Tr::NT) {
             const int row = idx / (Tr::DP - D), col = D + idx % (Tr::DP - D);
             Vs[row * Tr::LDV + col] = 0.f;
+            Vs[Tr::TILE_FLOATS + row * Tr::LDV + col] = 0.f;
         }
     }
 
@@ -277,29 +279,36 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
             }
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int buf) {
+        float* Kd = smem + buf * Tr::TILE_FLOATS;
+        float* Vd = Kd + Tr::KS_FLOATS;
 #pragma unroll
         for (int i = 0; i < Tr::PER; ++i) {
             const int idx = tid + Tr::NT * i;
             if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
                 const int row = idx / (D / 4), c4 = idx % (D / 4);
-                *(f32x4*)&Ks[row * Tr::LDK + 4 * c4] = kreg[i];
-                *(f32x4*)&Vs[row * Tr::LDV + 4 * c4] = vreg[i];
+                *(f32x4*)&Kd[row * Tr::LDK + 4 * c4] = kreg[i];
+                *(f32x4*)&Vd[row * Tr::LDV + 4 * c4] = vreg[i];
             }
         }
     };
 
+    // Two K/V buffers: while tile j is multiplied, tile j + 1 goes into the other buffer
+    // and tile j + 2 into registers, so one barrier per tile suffices (as in the forward).
     table(0);
     gload(0);
     table(Tr::BN);
+    lstore(0);
+    if (1 < ntiles) {
+        gload(Tr::BN);
+        table(2 * Tr::BN);
+    }
+    __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
-        __syncthreads();  // everyone is done reading the previous tile
-        lstore();
-        __syncthreads();
-        if (j + 1 < ntiles) {
-            gload((j + 1) * Tr::BN);
-            table((j + 2) * Tr::BN);
-        }
+        // tile j is in buffer j & 1; buffer (j + 1) & 1 was last read in iteration j - 1,
+        // which every wave finished before the barrier that ended it
+        Ks = smem + (j & 1) * Tr::TILE_FLOATS;
+        Vs = Ks + Tr::KS_FLOATS;
 
         const int kv0 = j * Tr::BN;
         // 16-key sub-tiles with a key <= this wave's last position
@@ -380,6 +389,14 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
                 }
             }
         }
+        if (j + 1 < ntiles) {
+            lstore((j + 1) & 1);
+            if (j + 2 < ntiles) {
+                gload((j + 2) * Tr::BN);
+                table((j + 3) * Tr::BN);
+            }
+        }
+        __syncthreads();
     }
 
     // Merge the two key halves through LDS (half 1 hands its state to half 0).
