@@ -309,7 +309,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
             float* dQh = dQ + hoff * D;
             {
                 const int q0 = qb * Tr::BM;
-                __syncthreads();  // the previous tile's LDS readers are done
+                // No barrier before these stores: every reader of the previous step's Q, dO
+                // and row statistics (the S/dP, softmax and dV/dK phases) came before that
+                // step's barrier after the dS store, and a segment starts with a barrier.
 #pragma unroll
                 for (int i = 0; i < PER; ++i) {
                     const int idx = tid + Tr::NT * i;
