@@ -47,7 +47,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 # HBM bytes per attn_causal_bwd launch on the 1024-token workload, from FETCH_SIZE (x2.00)
 # and WRITE_SIZE (x1.00) counter passes; valid only for the kernel source they were taken on.
 BWD_TRAFFIC_BYTES = 164.3e6
-BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "7eaa35e28691a248"
+BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "db5f1abcd149b373"
 CAUSAL = "mha_b4_h8_t1024_d64"
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"
 DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
