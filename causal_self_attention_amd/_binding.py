@@ -10,6 +10,7 @@ AttnError carrying the status code and the library's thread-local message, in
 the manner of the Python client on "Execution Backends and the Python ABI",
 "Python client".
 """
+import contextlib
 import ctypes
 import math
 import os
@@ -113,6 +114,15 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context for the tensors this module allocates for a call (outputs and
+    workspace): with an explicit stream they are allocated while that stream is
+    current, so torch's caching allocator hands their memory to later allocations
+    only in that stream's order -- after the call's kernels -- even when the
+    workspace is dropped as soon as the call returns."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
 def _dev(t, name, dtype=torch.float32):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -159,10 +169,11 @@ def attn_causal_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
     if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, T), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq, T), device=dev, dtype=torch.float32)
     _check(lib().attn_causal_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, T, D, scale,
                                  _dev(o, "o"), _dev(lse, "lse"), _stream_ptr(stream, dev)))
     return o, lse
@@ -177,15 +188,16 @@ def attn_causal_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None
     if v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, T):
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if dq is None:
-        dq = torch.empty_like(q)
-    if dk is None:
-        dk = torch.empty_like(k)
-    if dv is None:
-        dv = torch.empty_like(v)
     need = attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        if dq is None:
+            dq = torch.empty_like(q)
+        if dk is None:
+            dk = torch.empty_like(k)
+        if dv is None:
+            dv = torch.empty_like(v)
+        if workspace is None:
+            workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
     _check(lib().attn_causal_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(lse, "lse"),
                                  _dev(dout, "dout"), B, Hq, Hkv, T, D, scale, _dev(dq, "dq"),
                                  _dev(dk, "dk"), _dev(dv, "dv"), _dev(workspace, "workspace"),
@@ -205,13 +217,14 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
         raise ValueError("shape mismatch among q, pools, block_table, context_lens")
     max_pages = block_table.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if o is None:
-        o = torch.empty_like(q)
-    if with_lse and lse is None:
-        lse = torch.empty((S, Hq), device=dev, dtype=torch.float32)
     need = attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if with_lse and lse is None:
+            lse = torch.empty((S, Hq), device=dev, dtype=torch.float32)
+        if workspace is None:
+            workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
     lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
     _check(lib().attn_paged_decode(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                    _dev(block_table, "block_table", torch.int32),
@@ -235,12 +248,13 @@ def attn_materialized_fwd(q, k, v, scale=None, o=None, lse=None, p=None, stream=
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if o is None:
-        o = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, T), device=dev, dtype=torch.float32)
-    if p is None:
-        p = torch.empty((B, Hq, T, T), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, Hq, T), device=dev, dtype=torch.float32)
+        if p is None:
+            p = torch.empty((B, Hq, T, T), device=dev, dtype=torch.float32)
     _check(lib().attn_materialized_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), B, Hq, Hkv, T, D, scale,
                                        _dev(o, "o"), _dev(lse, "lse"), _dev(p, "p"), _stream_ptr(stream, dev)))
     return o, lse, p
@@ -255,12 +269,13 @@ def attn_materialized_bwd(q, k, v, o, p, dout, dp=None, scale=None, dq=None, dk=
     if p.shape != (B, Hq, T, T) or (dp is not None and dp.shape != p.shape):
         raise ValueError("p (and dp) must be [B, Hq, T, T]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
     need = attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
-    if workspace is None:
-        workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        if workspace is None:
+            workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
     dp_p = _dev(dp, "dp") if dp is not None else ctypes.c_void_p(0)
     _check(lib().attn_materialized_bwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(p, "p"),
                                        _dev(dout, "dout"), dp_p, B, Hq, Hkv, T, D, scale, _dev(dq, "dq"),
@@ -358,10 +373,11 @@ def attn_paged_prefill(q, k_pool, v_pool, block_table, context_lens, token_start
     if Dk != D or block_table.dim() != 2 or context_lens.shape != (S,) or token_start.shape != (S + 1,):
         raise ValueError("shape mismatch among q, pools, block_table, context_lens, token_start")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    if o is None:
-        o = torch.empty_like(q)
-    if with_lse and lse is None:
-        lse = torch.empty((N, Hq), device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty_like(q)
+        if with_lse and lse is None:
+            lse = torch.empty((N, Hq), device=dev, dtype=torch.float32)
     lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
     _check(lib().attn_paged_prefill(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                     _dev(block_table, "block_table", torch.int32),

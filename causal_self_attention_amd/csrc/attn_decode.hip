@@ -448,7 +448,9 @@ struct DecValuTraits {
     // per CU were slower (the memory system is already saturated by one group ahead)
     static constexpr int DEPTH = 16 / NP > 2 ? 16 / NP : 2;
 };
-constexpr float kDecodeNoMax = -1e30f;  // running max before any position: finite, so no inf - inf
+// running max before any position: the lowest finite float, so no inf - inf, and any
+// finite score (however negative) is above it and moves it
+constexpr float kDecodeNoMax = -3.402823466e38f;
 
 // sum over the ND lanes of a position (the low lane bits)
 template <int ND>

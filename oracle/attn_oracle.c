@@ -117,62 +117,91 @@ int oracle_causal_fwd(const double* q, const double* k, const double* v,
  * Delta_i = sum_j P_ij dP_ij (the chain rule through the row normalisation):
  *   dQ_i = scale * sum_{j<=i} dS_ij k_j
  *   dK_j = scale * sum_h sum_{i>=j} dS_ij q_i
- *   dV_j =         sum_h sum_{i>=j} P_ij dO_i                                */
+ *   dV_j =         sum_h sum_{i>=j} P_ij dO_i
+ * One query head at a time (in parallel over heads): its P and dS [T,T], its dQ,
+ * and its own share of dK and dV; the shares of a key/value head's query heads
+ * are then added in head order.  Every sum takes its terms in ascending index
+ * order (j for dQ, i for the shares, h for the group sum).                  */
 int oracle_causal_bwd(const double* q, const double* k, const double* v, const double* dout,
                       int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t D, double scale,
                       double* dq, double* dk, double* dv) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || T <= 0 || D <= 0 || Hq % Hkv != 0) return -1;
     const int64_t G = Hq / Hkv;
+    /* each query head's share of dK and dV: [B,Hq,T,D] */
+    double* dk_share = (double*)malloc((size_t)(B * Hq * T * D) * sizeof(double));
+    double* dv_share = (double*)malloc((size_t)(B * Hq * T * D) * sizeof(double));
+    if (!dk_share || !dv_share) { free(dk_share); free(dv_share); return -1; }
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t bg = 0; bg < B * Hkv; ++bg) {
-        const int64_t b = bg / Hkv, g = bg % Hkv;
-        const double* kg = k + (b * Hkv + g) * T * D;
-        const double* vg = v + (b * Hkv + g) * T * D;
-        double* dkg = dk + (b * Hkv + g) * T * D;
-        double* dvg = dv + (b * Hkv + g) * T * D;
-        memset(dkg, 0, (size_t)(T * D) * sizeof(double));
-        memset(dvg, 0, (size_t)(T * D) * sizeof(double));
+    for (int64_t bh = 0; bh < B * Hq; ++bh) {
+        const int64_t b = bh / Hq, h = bh % Hq, kvh = h / G;
+        const double* qh = q + bh * T * D;
+        const double* doh = dout + bh * T * D;
+        const double* kg = k + (b * Hkv + kvh) * T * D;
+        const double* vg = v + (b * Hkv + kvh) * T * D;
+        double* dqh = dq + bh * T * D;
+        double* dkh = dk_share + bh * T * D;
+        double* dvh = dv_share + bh * T * D;
         double* P = (double*)malloc((size_t)(T * T) * sizeof(double));
-        double* dS = (double*)malloc((size_t)(T * T) * sizeof(double));
+        double* dS = (double*)calloc((size_t)(T * T), sizeof(double));
         if (!P || !dS) { free(P); free(dS); failed = 1; continue; }
-        for (int64_t h = g * G; h < (g + 1) * G; ++h) {
-            const double* qh = q + (b * Hq + h) * T * D;
-            const double* doh = dout + (b * Hq + h) * T * D;
-            double* dqh = dq + (b * Hq + h) * T * D;
-            head_probabilities(qh, kg, T, D, scale, P, NULL);
-            for (int64_t i = 0; i < T; ++i) {
-                double delta = 0.0;
-                for (int64_t j = 0; j <= i; ++j) {
-                    double dp = 0.0;
-                    for (int64_t c = 0; c < D; ++c) dp += doh[i * D + c] * vg[j * D + c];
-                    dS[i * T + j] = dp;               /* dP for now */
-                    delta += P[i * T + j] * dp;
-                }
-                for (int64_t j = 0; j <= i; ++j) dS[i * T + j] = P[i * T + j] * (dS[i * T + j] - delta);
+        head_probabilities(qh, kg, T, D, scale, P, NULL);
+        for (int64_t i = 0; i < T; ++i) {
+            double delta = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dp = 0.0;
+                for (int64_t c = 0; c < D; ++c) dp += doh[i * D + c] * vg[j * D + c];
+                dS[i * T + j] = dp;               /* dP for now */
+                delta += P[i * T + j] * dp;
             }
-            for (int64_t i = 0; i < T; ++i) {
-                for (int64_t c = 0; c < D; ++c) {
-                    double acc = 0.0;
-                    for (int64_t j = 0; j <= i; ++j) acc += dS[i * T + j] * kg[j * D + c];
-                    dqh[i * D + c] = scale * acc;
-                }
+            for (int64_t j = 0; j <= i; ++j) dS[i * T + j] = P[i * T + j] * (dS[i * T + j] - delta);
+        }
+        /* dQ_i = scale * sum_{j<=i} dS_ij k_j */
+        for (int64_t i = 0; i < T; ++i) {
+            for (int64_t c = 0; c < D; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j <= i; ++j) acc += dS[i * T + j] * kg[j * D + c];
+                dqh[i * D + c] = scale * acc;
             }
-            for (int64_t j = 0; j < T; ++j) {
+        }
+        /* this head's share: sum_{i>=j} dS_ij q_i (times scale) and sum_{i>=j} P_ij dO_i,
+         * row i of dS and P adding its terms to every key j <= i, i ascending */
+        memset(dkh, 0, (size_t)(T * D) * sizeof(double));
+        memset(dvh, 0, (size_t)(T * D) * sizeof(double));
+        for (int64_t i = 0; i < T; ++i) {
+            for (int64_t j = 0; j <= i; ++j) {
+                const double dsij = dS[i * T + j], pij = P[i * T + j];
                 for (int64_t c = 0; c < D; ++c) {
-                    double acck = 0.0, accv = 0.0;
-                    for (int64_t i = j; i < T; ++i) {
-                        acck += dS[i * T + j] * qh[i * D + c];
-                        accv += P[i * T + j] * doh[i * D + c];
-                    }
-                    dkg[j * D + c] += scale * acck;
-                    dvg[j * D + c] += accv;
+                    dkh[j * D + c] += dsij * qh[i * D + c];
+                    dvh[j * D + c] += pij * doh[i * D + c];
                 }
             }
         }
+        for (int64_t e = 0; e < T * D; ++e) dkh[e] = scale * dkh[e];
         free(P);
         free(dS);
     }
+    /* dK, dV of key/value head g: the shares of its query heads g*G .. g*G+G-1 */
+    if (!failed) {
+#pragma omp parallel for schedule(static)
+        for (int64_t bg = 0; bg < B * Hkv; ++bg) {
+            const int64_t b = bg / Hkv, g = bg % Hkv;
+            double* dkg = dk + bg * T * D;
+            double* dvg = dv + bg * T * D;
+            memset(dkg, 0, (size_t)(T * D) * sizeof(double));
+            memset(dvg, 0, (size_t)(T * D) * sizeof(double));
+            for (int64_t h = g * G; h < (g + 1) * G; ++h) {
+                const double* dkh = dk_share + (b * Hq + h) * T * D;
+                const double* dvh = dv_share + (b * Hq + h) * T * D;
+                for (int64_t e = 0; e < T * D; ++e) {
+                    dkg[e] += dkh[e];
+                    dvg[e] += dvh[e];
+                }
+            }
+        }
+    }
+    free(dk_share);
+    free(dv_share);
     return failed ? -1 : 0;
 }
 

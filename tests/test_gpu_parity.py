@@ -3,10 +3,10 @@
 Tolerances (max-abs error relative to the reference's largest magnitude):
 O and LSE 1e-4, dQ/dK/dV 1e-3, paged decode vs dense decode 1e-5.
 
-Sizes the oracle finishes in seconds are compared element by element; the
-8192-token grouped-query forward is compared on sampled rows, each of which the
-oracle computes as a single-query decode over the row's causal prefix (the
-oracle's pins tie that decode to the last row of the causal forward).
+Every named workload is compared element by element on whole tensors, the
+8192-token grouped-query forward included (the oracle takes tens of seconds
+there); its rows are also checked against the oracle's single-query decode over
+the row's causal prefix, a second route through the definition.
 """
 import math
 
@@ -68,20 +68,23 @@ def test_workload_forward_backward(dev, orc, name):
 SAMPLE_ROWS = [0, 1, 15, 16, 63, 64, 65, 127, 128, 1000, 4095, 4096, 8127, 8128, 8190, 8191]
 
 
-def test_gqa_t8192_forward_sampled_rows(dev, orc):
-    name = "gqa_b1_hq16_hkv4_t8192_d64"
-    announce(f"fwd workload {name}")
-    host = si.causal_workload(name)
+def test_gqa_t8192_forward_whole(dev, gqa_t8192_reference, orc):
+    """Whole O [1,16,8192,64] and LSE [1,16,8192] against the oracle's causal forward,
+    and sampled rows against its single-query decode over the row's prefix."""
+    ref = gqa_t8192_reference
+    host = ref["host"]
+    announce("fwd workload gqa_b1_hq16_hkv4_t8192_d64 (whole tensors)")
     x = _to(host, dev)
-    o, lse = _run_fwd(x)
+    o, lse = _run_fwd(x, ref["scale"])
     o_h, lse_h = o.cpu(), lse.cpu()
-    assert torch.isfinite(o_h).all() and torch.isfinite(lse_h).all()
+    assert rel_err(o_h, ref["o"]) <= TOL_O, ("O", rel_err(o_h, ref["o"]))
+    assert rel_err(lse_h, ref["lse"]) <= TOL_LSE, ("LSE", rel_err(lse_h, ref["lse"]))
     rng = np.random.default_rng(4)
-    rows = sorted(set(SAMPLE_ROWS) | set(int(r) for r in rng.integers(0, 8192, 24)))
+    rows = sorted(set(SAMPLE_ROWS) | set(int(r) for r in rng.integers(0, 8192, 8)))
     q, k, v = host["q"][0], host["k"][0], host["v"][0]  # [H, T, D]
     for i in rows:
         ro, rlse = orc.decode_dense(q[:, i, :], k[:, : i + 1, :].transpose(0, 1), v[:, : i + 1, :].transpose(0, 1),
-                                    1.0 / 8.0)
+                                    ref["scale"])
         assert rel_err(o_h[0, :, i, :], ro) <= TOL_O, ("O row", i, rel_err(o_h[0, :, i, :], ro))
         assert rel_err(lse_h[0, :, i], rlse) <= TOL_LSE, ("LSE row", i)
 
@@ -440,6 +443,46 @@ def test_decode_split_many_sequences(dev, orc):
     ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"])
     assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
     assert rel_err(lse, rlse) <= TOL_DECODE
+
+
+@pytest.mark.parametrize("path,G", [("split", 4), ("split", 1), ("split", 8), ("fused", 4)])
+def test_decode_large_negative_logits(dev, orc, path, G):
+    """Every score of every head far below -1e30 (scale 1e32, q.k < 0): softmax is
+    still defined (one-hot on each head's largest score), so O is that key's value
+    row and LSE that score, on every decode path (the VALU split kernel for G <= 4,
+    the MFMA one above, the fused one for more than 1024 sequences)."""
+    Hkv, D, ps = 2, 64, 16
+    S = _decode_batch(dev, path, Hkv)
+    announce(f"decode large negative logits {path} S={S} G={G}")
+    d = si.paged_decode_inputs(S=S, Hq=Hkv * G, Hkv=Hkv, D=D, page_size=ps, ctx_lo=1,
+                               ctx_hi=300 if path == "split" else 40, max_pages=math.ceil(300 / ps), seed=130 + G)
+    d["q"] = -d["q"].abs()
+    kp = d["k_pool"].abs() + 0.01
+    # one position per sequence gets a key a quarter as long, so its score is the
+    # largest by a wide margin for every query head (fp32 and fp64 then agree on
+    # the argmax whatever the rounding of the dot products)
+    for s in range(S):
+        n = int(d["context_lens"][s])
+        t = (7919 * s) % n
+        kp[int(d["block_table"][s, t // ps]), :, t % ps] *= 0.25
+    d["k_pool"] = kp
+    scale = 1e32
+    for s in range(S):
+        n = int(d["context_lens"][s])
+        if n < 2:
+            continue
+        pos = torch.arange(n)
+        rows = d["block_table"][s, pos // ps].long()
+        kk = kp[rows, :, pos % ps].double()  # [n, Hkv, D]
+        sc = torch.einsum("nhd,hgd->nhg", kk, d["q"][s].double().reshape(Hkv, G, D)).reshape(n, -1)
+        top = torch.topk(sc, 2, dim=0).values
+        assert float((top[0] - top[1]).min()) > 1e-3 * float(sc.abs().max()), s
+    o, lse = _decode(d, dev, scale=scale)
+    ro, rlse = orc.paged_decode(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"], scale)
+    assert float(np.max(rlse)) < -1e30
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    assert rel_err(o, ro) <= TOL_DECODE, ("O", rel_err(o, ro))
+    assert rel_err(lse, rlse) <= TOL_DECODE, ("LSE", rel_err(lse, rlse))
 
 
 def test_decode_shared_workspace(dev, orc):

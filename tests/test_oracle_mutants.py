@@ -37,12 +37,14 @@ MUTANTS = {
     "delta_without_P": ("delta += P[i * T + j] * dp;", "delta += dp;"),
     "dS_sign": ("P[i * T + j] * (dS[i * T + j] - delta)", "P[i * T + j] * (delta - dS[i * T + j])"),
     "dQ_no_scale": ("dqh[i * D + c] = scale * acc;", "dqh[i * D + c] = acc;"),
-    "dK_transposed_dS": ("acck += dS[i * T + j] * qh[i * D + c];",
-                         "acck += dS[j * T + i] * qh[i * D + c];"),
-    "dV_transposed_P": ("accv += P[i * T + j] * doh[i * D + c];",
-                        "accv += P[j * T + i] * doh[i * D + c];"),
-    "dV_not_group_summed": ("dvg[j * D + c] += accv;", "dvg[j * D + c] = accv;"),
-    "dK_not_group_summed": ("dkg[j * D + c] += scale * acck;", "dkg[j * D + c] = scale * acck;"),
+    "dK_transposed_dS": ("const double dsij = dS[i * T + j], pij = P[i * T + j];",
+                         "const double dsij = dS[j * T + i], pij = P[i * T + j];"),
+    "dV_transposed_P": ("const double dsij = dS[i * T + j], pij = P[i * T + j];",
+                        "const double dsij = dS[i * T + j], pij = P[j * T + i];"),
+    "dV_not_group_summed": ("dvg[e] += dvh[e];", "dvg[e] = dvh[e];"),
+    "dK_not_group_summed": ("dkg[e] += dkh[e];", "dkg[e] = dkh[e];"),
+    "dK_no_scale": ("for (int64_t e = 0; e < T * D; ++e) dkh[e] = scale * dkh[e];", ""),
+    "gqa_modulo_heads_bwd": ("h = bh % Hq, kvh = h / G;", "h = bh % Hq, kvh = h % Hkv;"),
     "bwd_strided_groups": ("for (int64_t h = g * G; h < (g + 1) * G; ++h)",
                            "for (int64_t h = g; h < Hq; h += Hkv)"),
     "decode_no_scale": ("p[t] = scale * s;", "p[t] = s;"),
