@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     ATTN_KV_SEQUENCE_FULL,
     ATTN_KV_STACK_OVERFLOW,
     ATTN_OK,
+    ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES,
     ATTN_UNSUPPORTED,
     ATTN_WORKSPACE_TOO_SMALL,
     AttnError,
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
     attn_materialized_bwd_workspace_bytes,
     attn_materialized_fwd,
     attn_paged_decode,
+    attn_paged_decode_noalloc,
     attn_paged_decode_workspace_bytes,
     attn_paged_prefill,
     lib,

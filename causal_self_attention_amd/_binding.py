@@ -25,7 +25,7 @@ ATTN_INVALID_ARGUMENT = 1
 ATTN_UNSUPPORTED = 2
 ATTN_WORKSPACE_TOO_SMALL = 3
 ATTN_DEVICE_ERROR = 4
-ATTN_ABI_VERSION = 0x00010003
+ATTN_ABI_VERSION = 0x00010004
 
 ATTN_KV_OK = 0
 ATTN_KV_POOL_EXHAUSTED = 1
@@ -56,6 +56,8 @@ SIGNATURES = {
     "attn_paged_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "attn_paged_decode": (_st, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _f, _vp, _vp, _vp, _sz, _vp]),
+    "attn_paged_decode_noalloc": (_st, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        _f, _vp, _vp, _vp]),
     "attn_materialized_fwd": (_st, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f, _vp, _vp, _vp, _vp]),
     "attn_materialized_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "attn_materialized_bwd": (_st, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f,
@@ -233,6 +235,33 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
                                    _dev(workspace, "workspace"),
                                    workspace.numel() * workspace.element_size(),
                                    _stream_ptr(stream, dev)))
+    return o, lse
+
+
+ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, context_lens, o, lse=None, scale=None, stream=None):
+    """attn_paged_decode with no workspace: the library's static per-GPU scratch holds
+    the partial results, and nothing is allocated, here or in the library (the caller
+    passes the outputs o [S,Hq,D] and, optionally, lse [S,Hq]).  Calls on one GPU share
+    that scratch, so overlapping calls race."""
+    _same_device(q, k_pool, v_pool, block_table, context_lens, o)
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("expected q [S,Hq,D] and pools [num_pages,Hkv,page_size,D]")
+    S, Hq, D = q.shape
+    num_pages, Hkv, page_size, Dk = k_pool.shape
+    if Dk != D or block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("shape mismatch among q, pools, block_table, context_lens")
+    if o.shape != q.shape or (lse is not None and lse.shape != (S, Hq)):
+        raise ValueError("o must be [S,Hq,D] and lse [S,Hq]")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
+    _check(lib().attn_paged_decode_noalloc(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                           _dev(block_table, "block_table", torch.int32),
+                                           _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D,
+                                           page_size, block_table.shape[1], num_pages, scale, _dev(o, "o"), lse_p,
+                                           _stream_ptr(stream, q.device)))
     return o, lse
 
 

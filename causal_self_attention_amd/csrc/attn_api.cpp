@@ -216,52 +216,119 @@ size_t attn_paged_decode_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int
     return (bytes + 255) / 256 * 256;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode calls, except for the workspace: sizes, the kernels'
+// shape support and the pointers.
+attn_status check_decode(const float* q, const float* k_pool, const float* v_pool, const int32_t* block_table,
+                         const int32_t* context_lens, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                         int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages, float scale, float* o,
+                         float* lse) {
+    if (S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+        return fail(ATTN_INVALID_ARGUMENT,
+                    "S, Hq, Hkv, D, page_size, max_pages_per_seq and num_pages must all be positive");
+    if (Hq % Hkv != 0)
+        return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads");
+    if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
+    if (page_size * max_pages_per_seq >= kMaxElems || S * Hq >= kMaxElems ||
+        num_pages * Hkv * page_size * D >= ((int64_t)1 << 40))
+        return fail(ATTN_INVALID_ARGUMENT, "sizes too large: page_size*max_pages_per_seq must stay below 2^31");
+    if (!attn::decode_shape_supported(D, page_size, Hq / Hkv))
+        return fail(ATTN_UNSUPPORTED, "no decode kernel for D=" + std::to_string(D) + ", page_size=" +
+                                          std::to_string(page_size) + ", Hq/Hkv=" + std::to_string(Hq / Hkv) +
+                                          " (supported: D in {8,16,32,64,128}, page_size in {16,32,64}, "
+                                          "1 <= Hq/Hkv <= 16)");
+    ATTN_TRY(check_ptr(q, "q", 16));
+    ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
+    ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
+    ATTN_TRY(check_ptr(block_table, "block_table", 4));
+    ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
+    ATTN_TRY(check_ptr(o, "o", 16));
+    if (lse) ATTN_TRY(check_ptr(lse, "lse", 4));
+    return ATTN_OK;
+}
+
+// The decode outputs (and the caller's workspace, `ws`, possibly empty) overlap no input
+// and no other output.
+attn_status check_decode_disjoint(const float* q, const float* k_pool, const float* v_pool,
+                                  const int32_t* block_table, const int32_t* context_lens, int64_t S, int64_t Hq,
+                                  int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages_per_seq,
+                                  int64_t num_pages, float* o, float* lse, Range ws) {
+    const size_t qb = (size_t)(S * Hq * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
+    const size_t tb = (size_t)(S * max_pages_per_seq) * 4, cb = (size_t)S * 4, lb = (size_t)(S * Hq) * 4;
+    const Range lr{lse, lse ? lb : 0, "lse"};
+    return check_disjoint({{o, qb, "o"}, lr, ws},
+                          {{q, qb, "q"}, {k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
+                           {block_table, tb, "block_table"}, {context_lens, cb, "context_lens"}});
+}
+
+}  // namespace
+
+extern "C" {
+
 attn_status attn_paged_decode(const float* q, const float* k_pool, const float* v_pool, const int32_t* block_table,
                               const int32_t* context_lens, int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
                               int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages, float scale, float* o,
                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     try {
-        if (S <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || page_size <= 0 || max_pages_per_seq <= 0 || num_pages <= 0)
-            return fail(ATTN_INVALID_ARGUMENT,
-                        "S, Hq, Hkv, D, page_size, max_pages_per_seq and num_pages must all be positive");
-        if (Hq % Hkv != 0)
-            return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads");
-        if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
-        if (page_size * max_pages_per_seq >= kMaxElems || S * Hq >= kMaxElems ||
-            num_pages * Hkv * page_size * D >= ((int64_t)1 << 40))
-            return fail(ATTN_INVALID_ARGUMENT, "sizes too large: page_size*max_pages_per_seq must stay below 2^31");
-        if (!attn::decode_shape_supported(D, page_size, Hq / Hkv))
-            return fail(ATTN_UNSUPPORTED, "no decode kernel for D=" + std::to_string(D) + ", page_size=" +
-                                              std::to_string(page_size) + ", Hq/Hkv=" + std::to_string(Hq / Hkv) +
-                                              " (supported: D in {8,16,32,64,128}, page_size in {16,32,64}, "
-                                              "1 <= Hq/Hkv <= 16)");
-        ATTN_TRY(check_ptr(q, "q", 16));
-        ATTN_TRY(check_ptr(k_pool, "k_pool", 16));
-        ATTN_TRY(check_ptr(v_pool, "v_pool", 16));
-        ATTN_TRY(check_ptr(block_table, "block_table", 4));
-        ATTN_TRY(check_ptr(context_lens, "context_lens", 4));
-        ATTN_TRY(check_ptr(o, "o", 16));
-        if (lse) ATTN_TRY(check_ptr(lse, "lse", 4));
+        ATTN_TRY(check_decode(q, k_pool, v_pool, block_table, context_lens, S, Hq, Hkv, D, page_size,
+                              max_pages_per_seq, num_pages, scale, o, lse));
         ATTN_TRY(check_ptr(workspace, "workspace", 16));
         const size_t need = attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages_per_seq);
         if (workspace_bytes < need)
             return fail(ATTN_WORKSPACE_TOO_SMALL, "workspace has " + std::to_string(workspace_bytes) +
                                                       " bytes, attn_paged_decode needs " + std::to_string(need));
-        const size_t qb = (size_t)(S * Hq * D) * 4, pb = (size_t)(num_pages * Hkv * page_size * D) * 4;
-        const size_t tb = (size_t)(S * max_pages_per_seq) * 4, cb = (size_t)S * 4, lb = (size_t)(S * Hq) * 4;
-        const Range lr{lse, lse ? lb : 0, "lse"};
-        ATTN_TRY(check_disjoint({{o, qb, "o"}, lr, {workspace, need, "workspace"}},
-                                {{q, qb, "q"}, {k_pool, pb, "k_pool"}, {v_pool, pb, "v_pool"},
-                                 {block_table, tb, "block_table"}, {context_lens, cb, "context_lens"}}));
+        ATTN_TRY(check_decode_disjoint(q, k_pool, v_pool, block_table, context_lens, S, Hq, Hkv, D, page_size,
+                                       max_pages_per_seq, num_pages, o, lse, Range{workspace, need, "workspace"}));
         int cus = 0;
         ATTN_TRY(device_ready(&cus));
         attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, (float*)workspace,
-                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale, cus};
+                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale, cus,
+                           attn::decode_workspace_slots(S)};
         return launched(attn::launch_paged_decode(a, (hipStream_t)stream), "attn_paged_decode launch");
     } catch (const std::exception& e) {
         return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_decode: ") + e.what());
     } catch (...) {
         return fail(ATTN_DEVICE_ERROR, "attn_paged_decode: unknown exception");
+    }
+}
+
+attn_status attn_paged_decode_noalloc(const float* q, const float* k_pool, const float* v_pool,
+                                      const int32_t* block_table, const int32_t* context_lens, int64_t S, int64_t Hq,
+                                      int64_t Hkv, int64_t D, int64_t page_size, int64_t max_pages_per_seq,
+                                      int64_t num_pages, float scale, float* o, float* lse, void* stream) {
+    try {
+        ATTN_TRY(check_decode(q, k_pool, v_pool, block_table, context_lens, S, Hq, Hkv, D, page_size,
+                              max_pages_per_seq, num_pages, scale, o, lse));
+        ATTN_TRY(check_decode_disjoint(q, k_pool, v_pool, block_table, context_lens, S, Hq, Hkv, D, page_size,
+                                       max_pages_per_seq, num_pages, o, lse, Range{nullptr, 0, "scratch"}));
+        int cus = 0;
+        ATTN_TRY(device_ready(&cus));
+        const int64_t slots = attn::decode_scratch_slots(S, Hkv, cus);
+        const size_t need = attn::decode_scratch_floats(S, Hq, D, slots);
+        if (slots > 0 && need > attn::decode_scratch_capacity_floats())
+            return fail(ATTN_WORKSPACE_TOO_SMALL,
+                        "attn_paged_decode_noalloc: this batch needs " + std::to_string(need * 4) +
+                            " bytes of scratch, the library's static scratch holds " +
+                            std::to_string(attn::decode_scratch_capacity_floats() * 4) +
+                            " (fewer sequences, query heads or head dims fit; attn_paged_decode takes a "
+                            "caller workspace of any size)");
+        float* scratch = nullptr;
+        if (slots > 0) {
+            const hipError_t e = attn::decode_scratch_address(&scratch);
+            if (e != hipSuccess)
+                return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_decode_noalloc: scratch address: ") +
+                                                   hipGetErrorString(e));
+        }
+        attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, scratch,
+                           S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale, cus, slots};
+        return launched(attn::launch_paged_decode(a, (hipStream_t)stream), "attn_paged_decode_noalloc launch");
+    } catch (const std::exception& e) {
+        return fail(ATTN_DEVICE_ERROR, std::string("attn_paged_decode_noalloc: ") + e.what());
+    } catch (...) {
+        return fail(ATTN_DEVICE_ERROR, "attn_paged_decode_noalloc: unknown exception");
     }
 }
 

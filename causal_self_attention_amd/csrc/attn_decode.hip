@@ -32,6 +32,8 @@
 // For more sequences than the split's partition holds (1024) a single fused kernel
 // takes a whole (sequence, KV head) pair per work-group instead.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "attn_launch.h"
 #include "device_common.h"
@@ -809,15 +811,74 @@ bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group) {
 // Workspace (floats): partial slots -- o [slots][Hq][D], then m and l [slots][Hq] -- for
 // at most the grid plus the sequences, then each sequence's first slot and slot count
 // (2 x S int32).
+size_t decode_scratch_floats(int64_t S, int64_t Hq, int64_t D, int64_t slots) {
+    return (size_t)(slots * Hq * (D + 2) + 2 * S);
+}
+int64_t decode_workspace_slots(int64_t S) { return kDecodeMaxWgs + S; }
 size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages) {
     (void)Hkv;
     (void)page_size;
     (void)max_pages;
-    return (size_t)((kDecodeMaxWgs + S) * Hq * (D + 2) + 2 * S);
+    return decode_scratch_floats(S, Hq, D, decode_workspace_slots(S));
 }
 
 bool decode_split_supported(int64_t S) { return S <= 64 * kDecodeScanChunks; }
+
+// Work-groups of the split grid on a device with cu_count compute units: kDecodeWaves
+// KV heads per work-group (gy work-groups across the KV heads), kDecodeWavesPerCu waves
+// per CU in all.
+static int decode_split_wgs(int64_t Hkv, int cu_count, int* wpw_out, int* gy_out) {
+    const int wpw = (int)std::min<int64_t>(Hkv, kDecodeWaves);
+    const int gy = (int)((Hkv + wpw - 1) / wpw);
+    if (wpw_out) *wpw_out = wpw;
+    if (gy_out) *gy_out = gy;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(kDecodeMaxWgs, (int64_t)kDecodeWavesPerCu * cu_count / (wpw * gy)));
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (attn_paged_decode_noalloc): the
+// split path's partials live here instead of in a caller workspace.  Every GPU the
+// library runs on holds its own copy for the life of the process; calls on one GPU
+// share it, so calls that overlap in time on one GPU race.  Host code never uses the
+// array's name as an address: it uses the device address that hipGetSymbolAddress
+// returns, looked up once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kDecodeScratchFloats = ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES / sizeof(float);
+static __device__ __align__(256) float scratch[kDecodeScratchFloats];
+
+size_t decode_scratch_capacity_floats() { return kDecodeScratchFloats; }
+
+int64_t decode_scratch_slots(int64_t S, int64_t Hkv, int cu_count) {
+    if (!decode_split_supported(S)) return 0;  // the fused path uses no workspace
+    return decode_split_wgs(Hkv, cu_count, nullptr, nullptr) + S;
+}
+
+constexpr int kScratchDevices = 64;
+static std::atomic<float*> g_scratch_addr[kScratchDevices];
+static std::mutex g_scratch_mutex;
+
+hipError_t decode_scratch_address(float** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    float* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void* addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));  // with device `dev` current
+            if (e != hipSuccess) return e;
+            if (!addr) return hipErrorInvalidSymbol;
+            p = (float*)addr;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 // measured: the balanced split beats one work-group per (sequence, KV head) from 32 up to
 // 256 sequences (e.g. 57.8 vs 71.4 us at 64, 218 vs 246 us at 256 sequences of 512..4096
 // positions), so it is used whenever its partition fits
@@ -834,11 +895,10 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
         return hipGetLastError();
     }
     // The positions of all sequences in equal shares over the whole chip, then the merge.
-    const int wpw = (int)std::min<int64_t>(a.Hkv, kDecodeWaves);  // waves (KV heads) per work-group
-    const int gy = (int)((a.Hkv + wpw - 1) / wpw);
-    const int nwg = (int)std::max<int64_t>(
-        1, std::min<int64_t>(kDecodeMaxWgs, (int64_t)kDecodeWavesPerCu * a.cu_count / (wpw * gy)));
-    const int64_t slots = kDecodeMaxWgs + a.S;
+    int wpw = 1, gy = 1;  // waves (KV heads) per work-group, work-groups across the KV heads
+    const int nwg = decode_split_wgs(a.Hkv, a.cu_count, &wpw, &gy);
+    const int64_t slots = a.slots;  // the split writes at most nwg + S - 1 partials
+    if (slots < nwg + a.S) return hipErrorInvalidValue;
     float* Po = a.partial;
     float* Pm = Po + (size_t)(slots * a.Hq * D);
     float* Pl = Pm + (size_t)(slots * a.Hq);

@@ -44,7 +44,8 @@ struct DecodeArgs {
     float* partial;  // workspace (see decode_workspace_floats)
     int64_t S, Hq, Hkv, D, page_size, max_pages, num_pages;
     float scale;
-    int cu_count;  // compute units of the device (choice of the fused or the split path)
+    int cu_count;   // compute units of the device (choice of the fused or the split path)
+    int64_t slots;  // partial slots the workspace is laid out for (at least the split grid + S)
 };
 
 struct KvAppendArgs {
@@ -99,6 +100,17 @@ size_t bwd_workspace_floats(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64
 constexpr int64_t kBwdMaxRunWgs = 512;
 size_t decode_workspace_floats(int64_t S, int64_t Hq, int64_t Hkv, int64_t D, int64_t page_size,
                                int64_t max_pages);
+// Partial slots of the caller-workspace layout (device independent: the largest split grid).
+int64_t decode_workspace_slots(int64_t S);
+
+// The decode's own static scratch (for callers that cannot allocate): the slots the split
+// path needs on a device with cu_count compute units (0 when the fused path takes the
+// batch), the floats they occupy, the scratch's capacity in floats, and its address on
+// the current device (looked up once per device).
+int64_t decode_scratch_slots(int64_t S, int64_t Hkv, int cu_count);
+size_t decode_scratch_floats(int64_t S, int64_t Hq, int64_t D, int64_t slots);
+size_t decode_scratch_capacity_floats();
+hipError_t decode_scratch_address(float** ptr);
 
 hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream);

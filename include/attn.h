@@ -46,7 +46,8 @@
  *
  * Ownership and synchrony.  Every tensor pointer is a DEVICE pointer owned by
  * the caller; the library never allocates, frees or keeps a pointer after a call
- * returns.  Outputs are fully overwritten.  A call validates its arguments on the
+ * returns (the one buffer of its own, attn_paged_decode_noalloc's static scratch,
+ * is part of its loaded device code, not a per-call allocation).  Outputs are fully overwritten.  A call validates its arguments on the
  * host, enqueues its kernels on `stream` (a hipStream_t; NULL is the null
  * stream) and returns without waiting: results are ready when the stream reaches
  * that point.  Inputs must stay unchanged and alive until then.
@@ -65,7 +66,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 0x00010003u /* 1.3: major << 16 | minor */
+#define ATTN_ABI_VERSION 0x00010004u /* 1.4: major << 16 | minor */
 
 typedef int32_t attn_status;
 enum {
@@ -167,6 +168,31 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
                               int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
                               float scale, float* o, float* lse,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_paged_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace and allocates and frees nothing: the partial results of the split path
+ * go to a static scratch array of ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on, from its first use there until the process
+ * ends (its address is looked up once per device).  Arguments, outputs, device-side
+ * preconditions and results are those of attn_paged_decode (the same kernels).
+ * Up to 1024 sequences the batch needs
+ *   (W + S) * Hq * (D + 2) * 4 + 8 * S bytes of scratch, W = min(1024, 4 * CUs / (w * ceil(Hkv / w))),
+ * w = min(Hkv, 4) (CUs: the device's compute units; 4.5 MB for 32 sequences of 16
+ * query heads, d = 64, on 256 CUs); a batch that needs more returns
+ * ATTN_WORKSPACE_TOO_SMALL (attn_paged_decode takes a workspace of any size).  More
+ * than 1024 sequences need none.  The scratch's contents on entry do not matter.
+ * Every call on one GPU uses that GPU's one scratch array, so calls that overlap in
+ * time on one GPU (from several streams or threads) race and may give wrong results:
+ * order them, e.g. on one stream.
+ */
+#define ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_paged_decode_noalloc(const float* q, const float* k_pool, const float* v_pool,
+                                      const int32_t* block_table, const int32_t* context_lens,
+                                      int64_t S, int64_t Hq, int64_t Hkv, int64_t D,
+                                      int64_t page_size, int64_t max_pages_per_seq, int64_t num_pages,
+                                      float scale, float* o, float* lse, void* stream);
 
 /*
  * Batched prefill over a paged K/V cache, for a ragged batch: sequence s brings

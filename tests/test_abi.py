@@ -54,7 +54,7 @@ def test_header_is_c11_clean(tmp_path):
 
 
 def test_version_and_status_values(L):
-    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010003
+    assert attn.attn_abi_version() == attn.ATTN_ABI_VERSION == 0x00010004
     header = open(HEADER).read()
     for name in ("ATTN_OK", "ATTN_INVALID_ARGUMENT", "ATTN_UNSUPPORTED", "ATTN_WORKSPACE_TOO_SMALL",
                  "ATTN_DEVICE_ERROR"):
@@ -115,6 +115,14 @@ def _dec(L, S=2, Hq=4, Hkv=2, D=64, page=16, maxp=8, npages=16, scale=0.125, ws_
         ws_bytes = attn.attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page, maxp)
     return L.attn_paged_decode(p["q"], p["kp"], p["vp"], p["bt"], p["ctx"], S, Hq, Hkv, D, page, maxp, npages,
                                scale, p["o"], p["lse"], p["ws"], ws_bytes, None)
+
+
+def _decna(L, S=2, Hq=4, Hkv=2, D=64, page=16, maxp=8, npages=16, scale=0.125, **ptrs):
+    names = ["q", "kp", "vp", "bt", "ctx", "o", "lse"]
+    p = {n: _p(i) for i, n in enumerate(names)}
+    p.update(ptrs)
+    return L.attn_paged_decode_noalloc(p["q"], p["kp"], p["vp"], p["bt"], p["ctx"], S, Hq, Hkv, D, page, maxp,
+                                       npages, scale, p["o"], p["lse"], None)
 
 
 def _matf(L, B=1, Hq=2, Hkv=2, T=16, D=8, scale=0.35, **ptrs):
@@ -219,6 +227,27 @@ def test_decode_invalid_arguments(L):
     _expect(_dec(L, bt=ctypes.c_void_p(0x400000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
 
 
+def test_decode_noalloc_invalid_arguments(L):
+    """The no-allocation decode validates exactly like attn_paged_decode (less the
+    workspace) before any HIP call."""
+    _expect(_decna(L, bt=None), attn.ATTN_INVALID_ARGUMENT, "'block_table' is NULL")
+    _expect(_decna(L, o=None), attn.ATTN_INVALID_ARGUMENT, "'o' is NULL")
+    _expect(_decna(L, S=0), attn.ATTN_INVALID_ARGUMENT, "positive")
+    _expect(_decna(L, Hq=6, Hkv=4), attn.ATTN_INVALID_ARGUMENT, "Hq % Hkv")
+    _expect(_decna(L, page=8), attn.ATTN_UNSUPPORTED, "page_size=8")
+    _expect(_decna(L, D=48), attn.ATTN_UNSUPPORTED, "D=48")
+    _expect(_decna(L, scale=float("nan")), attn.ATTN_INVALID_ARGUMENT, "scale")
+    _expect(_decna(L, o=_p(1)), attn.ATTN_INVALID_ARGUMENT, "overlaps input 'k_pool'")
+    _expect(_decna(L, lse=_p(5)), attn.ATTN_INVALID_ARGUMENT, "overlap")  # lse == o
+    _expect(_decna(L, lse=ctypes.c_void_p(0x700000002)), attn.ATTN_INVALID_ARGUMENT, "aligned")
+
+
+def test_decode_noalloc_scratch_constant():
+    m = re.search(r"#define ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                  open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == attn.ATTN_PAGED_DECODE_NOALLOC_SCRATCH_BYTES
+
+
 def test_materialized_invalid_arguments(L):
     _expect(_matf(L, p=None), attn.ATTN_INVALID_ARGUMENT, "'p' is NULL")
     _expect(_matf(L, D=20), attn.ATTN_UNSUPPORTED, "D=20")
@@ -291,6 +320,8 @@ def test_valid_call_without_device_reports_device_error(L):
     _expect(_fwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_bwd(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_dec(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_decna(L), attn.ATTN_DEVICE_ERROR, "device")
+    _expect(_decna(L, lse=None), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_matf(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_matb(L), attn.ATTN_DEVICE_ERROR, "device")
     _expect(_matb(L, dp=None), attn.ATTN_DEVICE_ERROR, "device")
