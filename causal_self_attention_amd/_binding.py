@@ -116,13 +116,17 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _alloc_on(stream):
+def _alloc_on(stream, *given):
     """Context for the tensors this module allocates for a call (outputs and
     workspace): with an explicit stream they are allocated while that stream is
     current, so torch's caching allocator hands their memory to later allocations
     only in that stream's order -- after the call's kernels -- even when the
-    workspace is dropped as soon as the call returns."""
-    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+    workspace is dropped as soon as the call returns.  When the caller passed every
+    buffer (`given` holds them; None marks one to allocate) nothing is allocated,
+    and the stream switch, which costs microseconds of host time, is skipped."""
+    if stream is None or all(t is not None for t in given):
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
 
 
 def _dev(t, name, dtype=torch.float32):
@@ -171,7 +175,7 @@ def attn_causal_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
     if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
         raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    with _alloc_on(stream):
+    with _alloc_on(stream, o, lse):
         if o is None:
             o = torch.empty_like(q)
         if lse is None:
@@ -191,7 +195,7 @@ def attn_causal_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D)
-    with _alloc_on(stream):
+    with _alloc_on(stream, dq, dk, dv, workspace):
         if dq is None:
             dq = torch.empty_like(q)
         if dk is None:
@@ -220,7 +224,7 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
     max_pages = block_table.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages)
-    with _alloc_on(stream):
+    with _alloc_on(stream, o, lse if with_lse else o, workspace):
         if o is None:
             o = torch.empty_like(q)
         if with_lse and lse is None:
@@ -277,7 +281,7 @@ def attn_materialized_fwd(q, k, v, scale=None, o=None, lse=None, p=None, stream=
     B, Hq, T, D = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    with _alloc_on(stream):
+    with _alloc_on(stream, o, lse, p):
         if o is None:
             o = torch.empty_like(q)
         if lse is None:
@@ -299,7 +303,7 @@ def attn_materialized_bwd(q, k, v, o, p, dout, dp=None, scale=None, dq=None, dk=
         raise ValueError("p (and dp) must be [B, Hq, T, T]")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
-    with _alloc_on(stream):
+    with _alloc_on(stream, dq, dk, dv, workspace):
         dq = torch.empty_like(q) if dq is None else dq
         dk = torch.empty_like(k) if dk is None else dk
         dv = torch.empty_like(v) if dv is None else dv
@@ -402,7 +406,7 @@ def attn_paged_prefill(q, k_pool, v_pool, block_table, context_lens, token_start
     if Dk != D or block_table.dim() != 2 or context_lens.shape != (S,) or token_start.shape != (S + 1,):
         raise ValueError("shape mismatch among q, pools, block_table, context_lens, token_start")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    with _alloc_on(stream):
+    with _alloc_on(stream, o, lse if with_lse else o):
         if o is None:
             o = torch.empty_like(q)
         if with_lse and lse is None:

@@ -430,7 +430,9 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 // position costs 4 G D flops for 8 D bytes of K and V, i.e. G / 2 flops per byte:
 // at G <= 4 the VALU keeps up with HBM, while a 16x16x4 MFMA tile would pad the G
 // heads to 16 columns and spend most of its cycles on zeros.
-// Layout (ND = D / 8 lanes per position, NP = 64 / ND positions per step):
+// Layout (ND = D / 8 lanes per position, NP = min(64 / ND, 16) positions per step, so
+// a step stays inside one 16-position group; at D <= 16 the lanes past NP positions
+// only shadow the last one):
 //   lane = dq + ND * pl owns head dims 4dq .. 4dq+3 and D/2 + 4dq .. D/2 + 4dq+3 of
 //   position pl of the step, so each of its two float4 loads covers ND * 16
 //   contiguous bytes of a position row together with the other dq lanes;
@@ -438,17 +440,25 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 //   softmax: every lane keeps its own running max and sum over the positions it
 //   sees (pl, pl + NP, ...), so the loop needs no other cross-lane step; the max
 //   moves only when a score exceeds it by more than 2^8 (a rare wave-wide branch);
-//   O += p V: 8 FMAs per head into the lane's own dims;
-//   at the end of a sequence's share the NP position lanes are merged with the
-//   log-sum-exp rule and the share is written as one partial per query head.
+//   O += p V: 8 FMAs per head into the lane's own dims.
+// A wave streams its share of the groups as one list, whatever sequences it covers:
+// the page, the position in its sequence and the sequence of up to 64 groups are
+// resolved at once (lane j <-> group j of the span), and the K/V register ring runs on
+// across sequence boundaries.  Where a step starts a new sequence, the finished one's
+// position lanes are merged with the log-sum-exp rule and written as one partial per
+// query head; the new sequence's queries were loaded when the previous one started.
+// So a share that ends one sequence and starts the next pays no restart latency there
+// (measured: such shares ended about 2 us after the others when each sequence restarted
+// the table and K/V loads).
 template <int D, int GM>
 struct DecValuTraits {
-    static constexpr int ND = D / 8;    // lanes per position
-    static constexpr int NP = 64 / ND;  // positions per step
+    static constexpr int ND = D / 8;                        // lanes per position
+    static constexpr int NP = 64 / ND < 16 ? 64 / ND : 16;  // positions per step
+    static constexpr int SPG = 16 / NP;                     // steps per 16-position group
     // steps in the K/V register ring: one 16-position group (at least two steps);
     // measured at the 32-, 128- and 1024-sequence batches, deeper rings and more waves
     // per CU were slower (the memory system is already saturated by one group ahead)
-    static constexpr int DEPTH = 16 / NP > 2 ? 16 / NP : 2;
+    static constexpr int DEPTH = SPG > 2 ? SPG : 2;
 };
 // running max before any position: the lowest finite float, so no inf - inf, and any
 // finite score (however negative) is above it and moves it
@@ -463,7 +473,7 @@ __device__ __forceinline__ float sum_dims(float x) {
     if constexpr (ND >= 16) x += dpp_mov<kDppRor8>(x);       // the other half of the row
     return x;
 }
-// sum / max over the positions of a step (the lane bits above the ND lanes)
+// sum / max over the position lanes of a wave (the lane bits above the ND lanes)
 template <int ND>
 __device__ __forceinline__ float sum_positions(float x) {
     if constexpr (ND == 1) return wave_sum(x);
@@ -481,88 +491,60 @@ __device__ __forceinline__ float max_positions(float x) {
     return rows4_max(x);
 }
 
-// One wave's pass over positions [t_lo, t_hi) of one (sequence, KV head), t_lo a
-// multiple of 16 and t_hi - t_lo <= 1024: bt_lane holds the page of group j of the
-// span in lane j.  K/V loads run DEPTH - 1 steps ahead through a register ring and
-// are issued unconditionally (a step past the span re-reads its last position);
-// lanes past t_hi score -inf and their V is zeroed, so pool slots past the context
-// may hold anything.
-template <int D, int GM>
-__device__ __forceinline__ void decode_valu_span(const float* __restrict__ Kp, const float* __restrict__ Vp,
-                                                 int bt_lane, int Hkv, int kvh, int PS, int t_lo, int t_hi,
-                                                 const float (&q)[GM][8], float (&m)[GM], float (&l)[GM],
-                                                 float (&acc)[GM][8]) {
-    using Tr = DecValuTraits<D, GM>;
-    constexpr int ND = Tr::ND, NP = Tr::NP, DEPTH = Tr::DEPTH;
-    const int lane = threadIdx.x & 63;
-    const int dq = lane % ND;
-    const int pl = lane / ND;
-    const int nsteps = (t_hi - t_lo + NP - 1) / NP;
-    float kr[DEPTH][8], vr[DEPTH][8];
-    auto issue = [&](int k, int slot) {
-        const int t0 = t_lo + min(k, nsteps - 1) * NP;
-        const int t = min(t0 + pl, t_hi - 1);
-        int page;
-        if constexpr (NP <= 16) page = __builtin_amdgcn_readlane(bt_lane, (t0 - t_lo) >> 4);  // one group per step
-        else page = __shfl(bt_lane, (t - t_lo) >> 4);
-        const size_t off = (((size_t)page * Hkv + kvh) * PS + (t & (PS - 1))) * D + 4 * dq;
-        load_vec<4, true>(Kp + off, &kr[slot][0]);
-        load_vec<4, true>(Kp + off + D / 2, &kr[slot][4]);
-        load_vec<4, true>(Vp + off, &vr[slot][0]);
-        load_vec<4, true>(Vp + off + D / 2, &vr[slot][4]);
-    };
-    auto step = [&](int k, int slot) {
-        const bool valid = t_lo + k * NP + pl < t_hi;
-        float sc[GM];
+// x of lane l ^ (1 << BIT), for the position bits BIT <= 3 (DPP where an exchange
+// pattern exists, else the LDS crossbar); 4 and 5 go through the row-swap permutes.
+template <int BIT>
+__device__ __forceinline__ float lane_xor(float x) {
+    if constexpr (BIT == 0) return dpp_mov<kDppXor1>(x);
+    else if constexpr (BIT == 1) return dpp_mov<kDppXor2>(x);
+    else if constexpr (BIT == 3) return dpp_mov<kDppRor8>(x);  // rotating a 16-lane row by 8 swaps its halves
+    else return __shfl_xor(x, 1 << BIT);
+}
+
+// Reduce-scatter over the lane bits BIT .. 5 (the position lanes): on entry v[0 .. N)
+// are this lane's addends; each stage pairs lane l with l ^ (1 << bit), and the lane
+// whose bit is 0 keeps the sums of the lower half of the list, its partner those of
+// the upper half, so the list halves per stage.  On return v[0 .. max(N >> stages, 1))
+// hold the sums over all position lanes of entries base .. of the original list; once
+// one entry is left the remaining stages add it up whole (lanes then hold duplicates,
+// and `dup` has the bits of those stages set in the lanes that are not the first copy).
+// Far fewer cross-lane moves than a whole-wave sum per entry: N / 2 + N / 4 + ... instead
+// of N per stage.
+template <int BIT, int N, int V>
+__device__ __forceinline__ void scatter_sum_positions(float (&v)[V], int lane, int& base, int& dup) {
+    if constexpr (BIT < 6) {
+        if constexpr (N >= 2) {
+            constexpr int H = N / 2;
+            const bool hi = (lane >> BIT) & 1;
+            if constexpr (BIT >= 4) {
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            float x = 0.f;
+                for (int j = 0; j < H; ++j) {
+                    float a = v[j], b = v[H + j];
+                    if constexpr (BIT == 4) swap_rows16(a, b);  // row pairs (0, 1), (2, 3): row 0 gets [a0, a1]
+                    else swap_rows32(a, b);                     // half pairs: rows 0-1 get [a0-1, a2-3]
+                    v[j] = a + b;
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x = fmaf(kr[slot][i], q[h][i], x);
-            x = sum_dims<ND>(x);
-            sc[h] = valid ? x : -INFINITY;
-        }
-        bool need = false;
-#pragma unroll
-        for (int h = 0; h < GM; ++h) need |= sc[h] > m[h] + kLazyRescale;
-        if (__ballot(need)) {  // wave-uniform and rare: move the max of every lane to its max seen
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                const float mn = fmaxf(m[h], sc[h]);
-                const float al = exp2_hw(m[h] - mn);
-                m[h] = mn;
-                l[h] *= al;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+                for (int j = 0; j < H; ++j) {
+                    const float keep = hi ? v[H + j] : v[j];
+                    const float send = hi ? v[j] : v[H + j];
+                    v[j] = keep + lane_xor<BIT>(send);
+                }
             }
-        }
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = valid ? vr[slot][i] : 0.f;
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            const float p = exp2_hw(sc[h] - m[h]);  // 0 past the span
-            l[h] += p;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(p, v[i], acc[h][i]);
-        }
-    };
-    // Whole rounds of DEPTH steps, so the loop body has no branch around a step (the
-    // steps past the span are fully masked), and a scheduling barrier after each issue,
-    // so the loads leave in slot order: the compiler's load-count waits are then per
-    // ring slot, the same on loop entry as on the back edge (with the prologue's loads
-    // reordered, the entry state forced a wait for every older load into the loop).
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) {
-        issue(d, d);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int k0 = 0; k0 < nsteps; k0 += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            issue(k0 + d + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
-            __builtin_amdgcn_sched_barrier(0);
-            step(k0 + d, d);
+            base += hi ? H : 0;
+            scatter_sum_positions<BIT + 1, H, V>(v, lane, base, dup);
+        } else {
+            if constexpr (BIT >= 4) {
+                float a, b;
+                if constexpr (BIT == 4) pair_xor16(v[0], a, b);
+                else pair_xor32(v[0], a, b);
+                v[0] = a + b;
+            } else {
+                v[0] += lane_xor<BIT>(v[0]);
+            }
+            dup |= lane & (1 << BIT);
+            scatter_sum_positions<BIT + 1, 1, V>(v, lane, base, dup);
         }
     }
 }
@@ -577,7 +559,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
     float* __restrict__ Pm, float* __restrict__ Pl, int32_t* __restrict__ Meta, int S, int Hq, int Hkv, int PS,
     int max_pages, int num_pages, int nwg, float c2 /* scale * log2(e) */) {
     using Tr = DecValuTraits<D, GM>;
-    constexpr int ND = Tr::ND;
+    constexpr int ND = Tr::ND, NP = Tr::NP, SPG = Tr::SPG, DEPTH = Tr::DEPTH;
     extern __shared__ int4 dec_seq_info[];  // [waves][64 * NCH]
     const int w = wave_uniform(threadIdx.x >> 6);
     const int kvh = blockIdx.y * (blockDim.x >> 6) + w;
@@ -590,23 +572,17 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
     if (wg >= pt.nact) return;
     const int u_lo = wave_uniform((int)(((int64_t)wg * pt.total) / pt.nact));
     const int u_hi = wave_uniform((int)(((int64_t)(wg + 1) * pt.total) / pt.nact));
-    const int s_first = wave_uniform(pt.ended_by(u_lo, S));
+    int s_walk = wave_uniform(pt.ended_by(u_lo, S));  // the sequence of group u_lo
     pt.store(part, S);
     const int lane = threadIdx.x & 63;
     const int dq = lane % ND;
-    const int pl = lane / ND;
+    const int pl = min(lane / ND, NP - 1);  // lanes past NP positions shadow the last one
+    const bool lane_on = lane / ND < NP;
     const int G = Hq / Hkv;
-    for (int s = s_first; s < S; ++s) {
-        const int4 info = part[s];
-        const int ps = wave_uniform(info.x);
-        const int len = wave_uniform(info.y);
-        const int pe = ps + (len + 15) / 16;
-        if (ps >= u_hi) break;
-        const int a = max(ps, u_lo), e = min(pe, u_hi);
-        if (a >= e) continue;  // a sequence without positions
-        const int32_t* bt_row = BT + (size_t)s * max_pages;
-        int bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, a - ps, 1, min(64, e - a));
-        float q[GM][8];  // query heads kvh*G + h (zero for h >= G), scaled by c2
+    const int ps_log2 = __builtin_ctz(PS);
+
+    // queries of kvh's heads for sequence s, scaled by c2 (zero for h >= G)
+    auto load_q = [&](int s, float (&qq)[GM][8]) {
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             const float* qr = Qd + ((size_t)s * Hq + (size_t)kvh * G + min(h, G - 1)) * D + 4 * dq;
@@ -615,34 +591,39 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
             const float f = h < G ? c2 : 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                q[h][i] = x0[i] * f;
-                q[h][4 + i] = x1[i] * f;
+                qq[h][i] = x0[i] * f;
+                qq[h][4 + i] = x1[i] * f;
             }
         }
-        float m[GM], l[GM], acc[GM][8];
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            m[h] = kDecodeNoMax;
-            l[h] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-        }
-        for (int j0 = a - ps; j0 < e - ps; j0 += 64) {  // spans of at most 64 groups (one table load each)
-            if (j0 > a - ps) bt = decode_bt_lane(bt_row, max_pages, PS, num_pages, j0, 1, min(64, e - ps - j0));
-            decode_valu_span<D, GM>(Kp, Vp, bt, Hkv, kvh, PS, 16 * j0, min(16 * min(j0 + 64, e - ps), len), q, m,
-                                    l, acc);
-        }
-        // merge the position lanes: M = max m, L = sum 2^(m - M) l, o = sum 2^(m - M) o
+    };
+    float q[GM][8], qn[GM][8];  // the current sequence's queries, and the next one's
+    int qseq = s_walk, nseq = -1;
+    load_q(s_walk, q);  // before the table loads: the first sequence's queries
+    float m[GM], l[GM], acc[GM][8];
+    int cur = -1;  // the sequence whose running state m, l, acc hold
+
+    // the finished sequence s: merge the position lanes (M = max m, L = sum 2^(m - M) l,
+    // o = sum 2^(m - M) o) and write the share's partial into the sequence's slot.  The
+    // maxima and sums go whole-wave (all lanes end equal); the 8 GM output values are
+    // reduce-scattered, so each lane ends with a few consecutive dims of one head.
+    auto flush = [&](int s) {
+        constexpr int V = 8 * GM;      // values per lane: acc[h][i] at 8h + i
+        constexpr int LB = __builtin_ctz(ND);  // the lowest position bit of the lane index
+        constexpr int KEEP = (V >> (6 - LB)) > 0 ? (V >> (6 - LB)) : 1;  // values left per lane
+        float val[V];
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
             const float M = max_positions<ND>(m[h]);
             const float f = exp2_hw(m[h] - M);  // 0 for a lane that saw no position
             l[h] = sum_positions<ND>(l[h] * f);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[h][i] = sum_positions<ND>(acc[h][i] * f);
+            for (int i = 0; i < 8; ++i) val[8 * h + i] = acc[h][i] * f;
             m[h] = M;
         }
-        const int k = wg - pt.owner(ps);  // this partial's place among the sequence's
+        int base = 0, dup = 0;
+        scatter_sum_positions<LB, V, V>(val, lane, base, dup);
+        const int4 info = part[s];
+        const int k = wg - pt.owner(wave_uniform(info.x));  // this partial's place among the sequence's
         const int first = wave_uniform(info.z);
         const int nslots = wave_uniform(info.w);
         if (k == 0 && blockIdx.y == 0 && w == 0 && lane == 0) {  // one writer per sequence
@@ -650,24 +631,153 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
             Meta[2 * s + 1] = nslots;
         }
         const size_t hb = (size_t)(first + k) * Hq + (size_t)kvh * G;  // row of query head kvh * G
-        if (pl == 0) {
-#pragma unroll
-            for (int h = 0; h < GM; ++h) {
-                if (h < G) {
-                    float* dst = Po + (hb + h) * D + 4 * dq;
-                    *(f32x4*)dst = f32x4{acc[h][0], acc[h][1], acc[h][2], acc[h][3]};
-                    *(f32x4*)(dst + D / 2) = f32x4{acc[h][4], acc[h][5], acc[h][6], acc[h][7]};
-                }
+        // this lane holds entries base .. base + KEEP - 1: head base / 8, dims i = base % 8 ..
+        // (i < 4: 4dq + i, else D/2 + 4dq + i - 4), never across the two halves (KEEP | 8,
+        // base a multiple of KEEP)
+        const int h = base / 8, i0 = base % 8;
+        if (h < G && dup == 0) {
+            float* dst = Po + (hb + h) * D + (i0 < 4 ? 4 * dq + i0 : D / 2 + 4 * dq + i0 - 4);
+            if constexpr (KEEP == 8) {
+                *(f32x4*)dst = f32x4{val[0], val[1], val[2], val[3]};
+                *(f32x4*)(dst + D / 2) = f32x4{val[4], val[5], val[6], val[7]};
+            } else if constexpr (KEEP == 4) {
+                *(f32x4*)dst = f32x4{val[0], val[1], val[2], val[3]};
+            } else if constexpr (KEEP == 2) {
+                *(f32x2*)dst = f32x2{val[0], val[1]};
+            } else {
+                dst[0] = val[0];
             }
         }
 #pragma unroll
-        for (int h = 0; h < GM; ++h) {
-            if (h < G && lane == h) {
-                Pm[hb + h] = m[h];
-                Pl[hb + h] = l[h];
+        for (int hh = 0; hh < GM; ++hh) {
+            if (hh < G && lane == hh) {
+                Pm[hb + hh] = m[hh];
+                Pl[hb + hh] = l[hh];
+            }
+        }
+    };
+
+    for (int u0 = u_lo; u0 < u_hi; u0 += 64) {
+        const int ng = min(64, u_hi - u0);
+        // lane j: group u0 + j of the span (lanes past it repeat its last group), its
+        // sequence (the last one starting at or before it; empty ones are passed over),
+        // the group's first position in that sequence, the sequence's length and the
+        // group's physical page -- clamped to the table row and the pool, so a broken
+        // table can give wrong numbers but never an out-of-bounds read
+        const int u = u0 + min(lane, ng - 1);
+        int sl = s_walk;
+        while (sl + 1 < S && part[sl + 1].x <= u) ++sl;
+        const int4 info = part[sl];
+        const int gp0 = 16 * (u - info.x);
+        const int glen = info.y;
+        const int page = min(max(BT[(size_t)sl * max_pages + min(gp0 >> ps_log2, max_pages - 1)], 0), num_pages - 1);
+        s_walk = wave_uniform(__builtin_amdgcn_readlane(sl, 63));
+        const int nsteps = ng * SPG;
+
+        // K/V loads run DEPTH - 1 steps ahead through a register ring and are issued
+        // unconditionally (a step past the span re-reads its last one, positions past a
+        // sequence's length stay inside their page); such positions score -inf and their
+        // V is zeroed, so pool slots past a context may hold anything
+        float kr[DEPTH][8], vr[DEPTH][8];
+        auto issue = [&](int k, int slot) {
+            const int kk = min(k, nsteps - 1);
+            const int j = kk / SPG;
+            const int pg = __builtin_amdgcn_readlane(page, j);
+            const int t = __builtin_amdgcn_readlane(gp0, j) + (kk % SPG) * NP + pl;
+            const size_t off = (((size_t)pg * Hkv + kvh) * PS + (t & (PS - 1))) * D + 4 * dq;
+            load_vec<4, true>(Kp + off, &kr[slot][0]);
+            load_vec<4, true>(Kp + off + D / 2, &kr[slot][4]);
+            load_vec<4, true>(Vp + off, &vr[slot][0]);
+            load_vec<4, true>(Vp + off + D / 2, &vr[slot][4]);
+        };
+        auto step = [&](int k, int slot) {
+            const bool in = k < nsteps;
+            const int j = min(k, nsteps - 1) / SPG;
+            const int sj = __builtin_amdgcn_readlane(sl, j);
+            if (in && sj != cur) {  // wave-uniform: this step starts sequence sj
+                if (cur >= 0) flush(cur);
+                if (qseq != sj) {
+                    if (nseq == sj) {
+#pragma unroll
+                        for (int h = 0; h < GM; ++h)
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) q[h][i] = qn[h][i];
+                    } else {
+                        load_q(sj, q);
+                    }
+                    qseq = sj;
+                }
+                cur = sj;
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    m[h] = kDecodeNoMax;
+                    l[h] = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+                }
+                // the queries of the span's next sequence, ahead of its first step
+                const uint64_t later = __ballot(lane < ng && sl > sj);
+                if (later) {
+                    nseq = __builtin_amdgcn_readlane(sl, (int)__builtin_ctzll(later));
+                    load_q(nseq, qn);
+                }
+            }
+            const int t = __builtin_amdgcn_readlane(gp0, j) + (k % SPG) * NP + pl;
+            const bool valid = in && lane_on && t < __builtin_amdgcn_readlane(glen, j);
+            float sc[GM];
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                float x = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x = fmaf(kr[slot][i], q[h][i], x);
+                x = sum_dims<ND>(x);
+                sc[h] = valid ? x : -INFINITY;
+            }
+            bool need = false;
+#pragma unroll
+            for (int h = 0; h < GM; ++h) need |= sc[h] > m[h] + kLazyRescale;
+            if (__ballot(need)) {  // wave-uniform and rare: move the max of every lane to its max seen
+#pragma unroll
+                for (int h = 0; h < GM; ++h) {
+                    const float mn = fmaxf(m[h], sc[h]);
+                    const float al = exp2_hw(m[h] - mn);
+                    m[h] = mn;
+                    l[h] *= al;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+                }
+            }
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = valid ? vr[slot][i] : 0.f;
+#pragma unroll
+            for (int h = 0; h < GM; ++h) {
+                const float p = exp2_hw(sc[h] - m[h]);  // 0 for an invalid position
+                l[h] += p;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(p, v[i], acc[h][i]);
+            }
+        };
+        // Whole rounds of DEPTH steps, so the loop body has no branch around a step (the
+        // steps past the span are fully masked), and a scheduling barrier after each issue,
+        // so the loads leave in slot order: the compiler's load-count waits are then per
+        // ring slot, the same on loop entry as on the back edge (with the prologue's loads
+        // reordered, the entry state forced a wait for every older load into the loop).
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            issue(d, d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int k0 = 0; k0 < nsteps; k0 += DEPTH) {
+#pragma unroll
+            for (int d = 0; d < DEPTH; ++d) {
+                issue(k0 + d + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+                __builtin_amdgcn_sched_barrier(0);
+                step(k0 + d, d);
             }
         }
     }
+    if (cur >= 0) flush(cur);
 }
 
 // One wave per (sequence, query head) merges the sequence's partials with the
@@ -700,10 +810,15 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
         const int cv = min(64, n - c0);  // partials of this pass
         const size_t stat = (size_t)(first + c0 + min(lane, cv - 1)) * Hq + h;
         const float pm_ld = Pm[stat], pl_ld = Pl[stat];  // unconditional loads, masked below
+        // only the load instructions that reach a partial of the pass (a sequence usually
+        // has a handful: the work-groups its positions fall to)
         f32x4 x[NLD];
 #pragma unroll
-        for (int j = 0; j < NLD; ++j)
-            x[j] = *(const f32x4*)(Po + ((size_t)(first + c0 + min(j * RPI + rsub, cv - 1)) * Hq + h) * D + col);
+        for (int j = 0; j < NLD; ++j) {
+            x[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (j * RPI < cv)  // wave-uniform
+                x[j] = *(const f32x4*)(Po + ((size_t)(first + c0 + min(j * RPI + rsub, cv - 1)) * Hq + h) * D + col);
+        }
         const bool valid = lane < cv;
         const float pm = valid ? pm_ld : -INFINITY;
         const float m_new = fmaxf(M, wave_max(pm));  // finite: partial c0 exists
@@ -713,7 +828,8 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
         acc *= keep;
         M = m_new;
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) acc += __shfl(wl, j * RPI + rsub) * x[j];  // weight 0 past cv
+        for (int j = 0; j < NLD; ++j)
+            if (j * RPI < cv) acc += __shfl(wl, j * RPI + rsub) * x[j];  // weight 0 past cv
     }
 #pragma unroll
     for (int off = LPR; off < 64; off <<= 1) {
