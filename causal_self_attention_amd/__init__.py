@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     ATTN_WORKSPACE_TOO_SMALL,
     AttnError,
     PagedKvCache,
+    PreparedPagedDecode,
     attn_abi_version,
     attn_causal_bwd,
     attn_causal_bwd_workspace_bytes,

@@ -485,6 +485,25 @@ def test_decode_large_negative_logits(dev, orc, path, G):
     assert rel_err(lse, rlse) <= TOL_DECODE, ("LSE", rel_err(lse, rlse))
 
 
+def test_prepared_decode_reissues_the_same_call(dev):
+    """PreparedPagedDecode checks and marshals once; each call re-issues attn_paged_decode
+    on the same tensors, so new contents written into them between calls are picked up,
+    and every result equals the plain call's bit for bit."""
+    announce("prepared decode")
+    d = si.paged_decode_inputs(S=12, Hq=16, Hkv=4, D=64, page_size=16, ctx_lo=1, ctx_hi=900, max_pages=64, seed=24)
+    x = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    plan = attn.PreparedPagedDecode(x["q"], x["k_pool"], x["v_pool"], x["block_table"], x["context_lens"])
+    for i in range(3):
+        if i:
+            x["q"].mul_(-0.5).add_(0.25)  # new contents, same storage
+            x["context_lens"].sub_(1).clamp_(min=1)
+        o, lse = plan()
+        want_o, want_lse = attn.attn_paged_decode(x["q"], x["k_pool"], x["v_pool"], x["block_table"],
+                                                  x["context_lens"])
+        torch.cuda.synchronize()
+        assert torch.equal(o, want_o) and torch.equal(lse, want_lse), i
+
+
 def test_decode_shared_workspace(dev, orc):
     """Calls of different sizes sharing one workspace that starts out as NaN: its
     contents on entry do not matter, and each call's partials and slot records
