@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["attn_api.cpp", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_kv.hip", "attn_materialized.hip",
-           "attn_prefill.hip"]
+           "attn_prefill.hip", "attn_checks.hip"]
 ARCH = "gfx950"
 
 

@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
 #include "../../include/attn.h"
@@ -128,6 +129,54 @@ attn_status device_ready(int* cu_count) {
 attn_status launched(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTN_DEVICE_ERROR, std::string(what) + ": " + hipGetErrorString(e));
     return ok();
+}
+
+// ATTN_DEBUG_CHECKS=1 (read once per process) turns on the device-side checks of the
+// tables that paged decode and prefill read.
+bool debug_checks() {
+    static const bool on = [] {
+        const char* v = std::getenv("ATTN_DEBUG_CHECKS");
+        return v && v[0] == '1' && v[1] == 0;
+    }();
+    return on;
+}
+
+// Runs the table checks when they are on and the stream is not being captured into a
+// graph (a check waits for the stream, which capture forbids); a violation becomes
+// ATTN_INVALID_ARGUMENT naming the sequence and page, and nothing else is launched.
+attn_status debug_check_tables(const char* fn, const int32_t* ctx, const int32_t* bt, const int32_t* ts, int64_t S,
+                               int64_t N, int64_t max_pages, int64_t page_size, int64_t num_pages, int min_len,
+                               hipStream_t stream) {
+    if (!debug_checks()) return ATTN_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return fail(ATTN_DEVICE_ERROR, std::string(fn) + ": " + hipGetErrorString(e));
+    if (cap != hipStreamCaptureStatusNone) return ATTN_OK;
+    attn::TableCheck r{};
+    e = attn::check_paged_tables(ctx, bt, ts, S, N, max_pages, page_size, num_pages, min_len, stream, &r);
+    if (e != hipSuccess)
+        return fail(ATTN_DEVICE_ERROR, std::string(fn) + ": ATTN_DEBUG_CHECKS table check: " + hipGetErrorString(e));
+    const std::string s = std::to_string(r.seq);
+    switch (r.kind) {
+        case attn::kTableOk:
+            return ATTN_OK;
+        case attn::kTableBadLength:
+            return fail(ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": context_lens[" + s + "] = " + std::to_string(r.value) + " is outside [" +
+                            (ts ? "its new tokens" : "1") + ", max_pages_per_seq * page_size = " +
+                            std::to_string(max_pages * page_size) + "] (ATTN_DEBUG_CHECKS)");
+        case attn::kTableBadPage:
+            return fail(ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": block_table[" + s + ", " + std::to_string(r.page) + "] = " +
+                            std::to_string(r.value) + " is not a page of the pool (0 <= page < num_pages = " +
+                            std::to_string(num_pages) + ") (ATTN_DEBUG_CHECKS)");
+        case attn::kTableBadOffsets:
+            return fail(ATTN_INVALID_ARGUMENT,
+                        std::string(fn) + ": token_start is not nondecreasing from 0 to N at sequence " + s +
+                            " (value " + std::to_string(r.value) + ") (ATTN_DEBUG_CHECKS)");
+        default:
+            return fail(ATTN_DEVICE_ERROR, std::string(fn) + ": unknown table check result");
+    }
 }
 
 }  // namespace
@@ -284,6 +333,8 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
                                        max_pages_per_seq, num_pages, o, lse, Range{workspace, need, "workspace"}));
         int cus = 0;
         ATTN_TRY(device_ready(&cus));
+        ATTN_TRY(debug_check_tables("attn_paged_decode", context_lens, block_table, nullptr, S, 0, max_pages_per_seq,
+                                    page_size, num_pages, 1, (hipStream_t)stream));
         attn::DecodeArgs a{q, k_pool, v_pool, block_table, context_lens, o, lse, (float*)workspace,
                            S, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale, cus,
                            attn::decode_workspace_slots(S)};
@@ -315,6 +366,8 @@ attn_status attn_paged_decode_noalloc(const float* q, const float* k_pool, const
                             std::to_string(attn::decode_scratch_capacity_floats() * 4) +
                             " (fewer sequences, query heads or head dims fit; attn_paged_decode takes a "
                             "caller workspace of any size)");
+        ATTN_TRY(debug_check_tables("attn_paged_decode_noalloc", context_lens, block_table, nullptr, S, 0,
+                                    max_pages_per_seq, page_size, num_pages, 1, (hipStream_t)stream));
         float* scratch = nullptr;
         if (slots > 0) {
             const hipError_t e = attn::decode_scratch_address(&scratch);
@@ -543,6 +596,8 @@ attn_status attn_paged_prefill(const float* q, const float* k_pool, const float*
                                  {token_start, (size_t)(S + 1) * 4, "token_start"}}));
         int cus = 0;
         ATTN_TRY(device_ready(&cus));
+        ATTN_TRY(debug_check_tables("attn_paged_prefill", context_lens, block_table, token_start, S, N,
+                                    max_pages_per_seq, page_size, num_pages, 0, (hipStream_t)stream));
         attn::PrefillArgs a{q, k_pool, v_pool, block_table, context_lens, token_start, o, lse,
                             S, N, Hq, Hkv, D, page_size, max_pages_per_seq, num_pages, scale};
         return launched(attn::launch_paged_prefill(a, (hipStream_t)stream), "attn_paged_prefill launch");

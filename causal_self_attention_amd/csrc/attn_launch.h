@@ -112,6 +112,18 @@ size_t decode_scratch_floats(int64_t S, int64_t Hq, int64_t D, int64_t slots);
 size_t decode_scratch_capacity_floats();
 hipError_t decode_scratch_address(float** ptr);
 
+// Opt-in checks of the block tables, lengths and ragged offsets (ATTN_DEBUG_CHECKS=1):
+// the first violation, by sequence.  The call waits for the stream.
+enum { kTableOk = 0, kTableBadLength = 1, kTableBadPage = 2, kTableBadOffsets = 3 };
+struct TableCheck {
+    int32_t kind, seq, page, value;
+};
+// min_len: the smallest valid length (1 for decode, 0 for prefill, where a sequence
+// also needs at least its new tokens); ts may be NULL (decode).
+hipError_t check_paged_tables(const int32_t* ctx, const int32_t* bt, const int32_t* ts, int64_t S, int64_t N,
+                              int64_t max_pages, int64_t page_size, int64_t num_pages, int min_len,
+                              hipStream_t stream, TableCheck* out);
+
 hipError_t launch_causal_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_causal_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_materialized_fwd(const MatFwdArgs& a, hipStream_t stream);

@@ -161,6 +161,11 @@ size_t attn_paged_decode_workspace_bytes(int64_t S, int64_t Hq, int64_t Hkv, int
  * max_pages_per_seq * page_size and 0 <= block_table[s, p] < num_pages for
  * p < ceil(context_lens[s] / page_size).  Entries past that are never read, and
  * pool slots past a sequence's length are never used, so they may hold anything.
+ * A violated precondition gives wrong numbers but never an out-of-bounds access.
+ * With the environment variable ATTN_DEBUG_CHECKS=1 (read once per process) the call
+ * first checks them on the device and waits for the stream; a violation returns
+ * ATTN_INVALID_ARGUMENT naming the first offending sequence (and page) and nothing
+ * is launched.  The check is skipped while the stream is being captured into a graph.
  */
 attn_status attn_paged_decode(const float* q, const float* k_pool, const float* v_pool,
                               const int32_t* block_table, const int32_t* context_lens,
@@ -183,6 +188,7 @@ attn_status attn_paged_decode(const float* q, const float* k_pool, const float* 
  * query heads, d = 64, on 256 CUs); a batch that needs more returns
  * ATTN_WORKSPACE_TOO_SMALL (attn_paged_decode takes a workspace of any size).  More
  * than 1024 sequences need none.  The scratch's contents on entry do not matter.
+ * ATTN_DEBUG_CHECKS=1 checks the tables first, as for attn_paged_decode.
  * Every call on one GPU uses that GPU's one scratch array, so calls that overlap in
  * time on one GPU (from several streams or threads) race and may give wrong results:
  * order them, e.g. on one stream.
@@ -215,7 +221,8 @@ attn_status attn_paged_decode_noalloc(const float* q, const float* k_pool, const
  * Device-side preconditions (not checked on the host; violated ones give wrong
  * numbers but never an out-of-bounds access): the token_start properties above,
  * n_s <= context_lens[s] <= max_pages_per_seq * page_size, and table entries
- * below ceil(context_lens[s] / page_size) in [0, num_pages).
+ * below ceil(context_lens[s] / page_size) in [0, num_pages).  ATTN_DEBUG_CHECKS=1
+ * checks them first, as for attn_paged_decode.
  */
 attn_status attn_paged_prefill(const float* q, const float* k_pool, const float* v_pool,
                                const int32_t* block_table, const int32_t* context_lens,
