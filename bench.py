@@ -18,15 +18,17 @@ event, is reported beside it); `decode_sweep` adds the same shape with one
 16-position group per sequence (the fixed cost of a call), a 256-sequence batch,
 and the workload's rate beyond that fixed cost.  The 8192-token grouped-query forward and backward, the materialized path, a batched
 paged prefill of a ragged 8-sequence batch and the latency of a K/V append (the
-step before decode) are reported beside it.  Each decode call
-reads a different one of several pool replicas so the 256 MB last-level cache
-cannot serve a repeated pool.
+step before decode) are reported beside it, and so are the 16- and 256-token
+workloads' forward and backward times.  Each decode call reads a different one of
+several pool replicas so the 256 MB last-level cache cannot serve a repeated pool.
 
 `roofline` describes the dominant kernel (the backward: its delta/zero-fill
 pass plus the main KV-parallel kernel, launched together by attn_causal_bwd),
 measured with HIP events on the launch stream.  `cpu_baseline` is the CPU
 oracle (plain double-precision materialised attention) timed on this host on
-the full 1024-token forward+backward.
+the full 1024-token forward+backward; `cpu_oracle_beside` times it on the
+other workloads (the 8192-token forward once, the others as the median of 3)
+with the same algorithmic counts.
 """
 import argparse
 import json
@@ -49,6 +51,7 @@ PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 BWD_TRAFFIC_BYTES = 164.3e6
 BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "db5f1abcd149b373"
 CAUSAL = "mha_b4_h8_t1024_d64"
+SMALL = ("mha_b1_h2_t16_d8", "mha_b8_h4_t256_d32")
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"
 DECODE = "paged_decode_s32_hq16_hkv4_d64_p16"
 PREFILL = "paged_prefill_s8_hq16_hkv4_d64_p16"
@@ -102,8 +105,10 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only fill, sum and copy a buffer of this many MiB (plain kernels of known "
                          "traffic, to scale hardware byte counters) and exit")
-    ap.add_argument("--only", choices=["all", "bwd"], default="all",
-                    help="'bwd': run only the timed steps of forward + backward (for counter passes)")
+    ap.add_argument("--only", choices=["all", "bwd", "gqa", "decode"], default="all",
+                    help="'bwd': run only the timed steps of forward + backward; 'gqa': only the 8192-token "
+                         "grouped-query forward and backward, --gqa-iters times each; 'decode': only --steps "
+                         "decode calls on the pool replicas (for counter passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU (got --gpus {args.gpus}); "
@@ -132,6 +137,23 @@ def main():
         print(json.dumps({"calibrate_bytes": n * 4, "fill": 1, "sum": 3, "copy": 3}), flush=True)
         return
 
+    if args.only == "gqa":
+        gcfg = si.CAUSAL_WORKLOADS[GQA]
+        gh = si.causal_inputs(gcfg["B"], gcfg["Hq"], gcfg["Hkv"], gcfg["T"], gcfg["D"], gcfg["seed"], with_do=True)
+        gx = {k: v.to(dev) for k, v in gh.items()}
+        go = torch.empty_like(gx["q"])
+        glse = torch.empty((gcfg["B"], gcfg["Hq"], gcfg["T"]), device=dev)
+        gdq, gdk, gdv = torch.empty_like(gx["q"]), torch.empty_like(gx["k"]), torch.empty_like(gx["v"])
+        gws = torch.empty((attn.attn_causal_bwd_workspace_bytes(gcfg["B"], gcfg["Hq"], gcfg["Hkv"], gcfg["T"],
+                                                                gcfg["D"]) // 4,), device=dev)
+        for _ in range(args.gqa_iters):
+            attn.attn_causal_fwd(gx["q"], gx["k"], gx["v"], o=go, lse=glse, stream=stream)
+            attn.attn_causal_bwd(gx["q"], gx["k"], gx["v"], go, glse, gx["dout"], dq=gdq, dk=gdk, dv=gdv,
+                                 workspace=gws, stream=stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "gqa", "iters": args.gqa_iters}), flush=True)
+        return
+
     # ---- inputs and outputs, resident before timing ----
     cfg = si.CAUSAL_WORKLOADS[CAUSAL]
     B, Hq, Hkv, T, D = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["T"], cfg["D"]
@@ -158,6 +180,14 @@ def main():
                       device=dev)
     dbytes = decode_bytes(dh, dcfg["Hq"], dcfg["Hkv"], dcfg["D"])
     torch.cuda.synchronize()
+    if args.only == "decode":
+        plans = [attn.PreparedPagedDecode(dq_, kp, vp, bt, ctx, o=do_, lse=dlse, workspace=dws, stream=stream)
+                 for kp, vp in pools]
+        for i in range(args.steps):
+            plans[i % len(plans)]()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "decode", "calls": args.steps, "bytes_per_call": dbytes}), flush=True)
+        return
 
     def step(i, ev=None):
         if ev is not None:
@@ -374,6 +404,42 @@ def main():
     pre_us = statistics.median(a.elapsed_time(b) for a, b in pev[2:]) * 1e3
     del pdev, po, plse
 
+    # the 16- and 256-token workloads (parity cases, timed too): median over 20 calls of
+    # the forward and of the backward, events around each call (the 16-token one is a
+    # few microseconds of launches)
+    small = {}
+    for sname in SMALL:
+        sc = si.CAUSAL_WORKLOADS[sname]
+        sx = {k: v.to(dev) for k, v in si.causal_workload(sname).items()}
+        s_o = torch.empty_like(sx["q"])
+        s_l = torch.empty((sc["B"], sc["Hq"], sc["T"]), device=dev)
+        s_dq, s_dk, s_dv = torch.empty_like(sx["q"]), torch.empty_like(sx["k"]), torch.empty_like(sx["v"])
+        s_ws = torch.empty((max(attn.attn_causal_bwd_workspace_bytes(sc["B"], sc["Hq"], sc["Hkv"], sc["T"], sc["D"]),
+                                256) // 4,), device=dev)
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
+        torch.cuda.synchronize()
+        for it in range(25):
+            ev = sev[it - 5] if it >= 5 else None
+            if ev:
+                ev[0].record(stream)
+            attn.attn_causal_fwd(sx["q"], sx["k"], sx["v"], o=s_o, lse=s_l, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            attn.attn_causal_bwd(sx["q"], sx["k"], sx["v"], s_o, s_l, sx["dout"], dq=s_dq, dk=s_dk, dv=s_dv,
+                                 workspace=s_ws, stream=stream)
+            if ev:
+                ev[2].record(stream)
+        torch.cuda.synchronize()
+        f_us = statistics.median(e[0].elapsed_time(e[1]) for e in sev) * 1e3
+        b_us = statistics.median(e[1].elapsed_time(e[2]) for e in sev) * 1e3
+        sf, sb = causal_flops(sc["B"], sc["Hq"], sc["T"], sc["D"])
+        small[sname] = {"fwd_us_median": round(f_us, 2), "bwd_us_median": round(b_us, 2),
+                        "fwd_bwd_us": round(f_us + b_us, 2), "flops": sf + sb,
+                        "fwd_bwd_tflops": round((sf + sb) / ((f_us + b_us) * 1e-6) / 1e12, 4),
+                        "frac_of_fp32_mfma_peak": round((sf + sb) / ((f_us + b_us) * 1e-6) / 1e12
+                                                        / PEAK_FP32_MFMA_TFLOPS, 5)}
+        del sx, s_o, s_l, s_dq, s_dk, s_dv, s_ws
+
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -435,6 +501,7 @@ def main():
             "bwd_tflops": round(bwd_flops / (m_bwd_us * 1e-6) / 1e12, 3),
         },
         "decode_sweep": sweep,
+        "small_workloads": small,
         "paged_prefill": {
             "workload": PREFILL, "new_tokens": ph["N"], "us_median": round(pre_us, 2), "flops": p_flops,
             "tflops": round(p_flops / (pre_us * 1e-6) / 1e12, 3),
@@ -466,6 +533,41 @@ def main():
             "sample": f"full {CAUSAL} forward+backward (materialised, double), median of {len(runs)} runs, "
                       f"{cpu_s:.2f} s each; host {cpu_model()}",
         }
+
+        # the oracle beside the other workloads, same algorithmic counts as the GPU lines:
+        # the small ones and the decode one warm-up and the median of 3, the 8192-token
+        # forward one run
+        def med3(fn):
+            fn()
+            ts_ = []
+            for _ in range(3):
+                t = time.perf_counter()
+                fn()
+                ts_.append(time.perf_counter() - t)
+            return statistics.median(ts_)
+
+        beside = {"cores": orc.num_threads(), "host": cpu_model()}
+        for sname in SMALL:
+            hs = si.causal_workload(sname)
+            sc = si.CAUSAL_WORKLOADS[sname]
+            t_s = med3(lambda: (orc.causal_fwd(hs["q"], hs["k"], hs["v"]),
+                                orc.causal_bwd(hs["q"], hs["k"], hs["v"], hs["dout"])))
+            sf, sb = causal_flops(sc["B"], sc["Hq"], sc["T"], sc["D"])
+            beside[sname] = {"fwd_bwd_s": round(t_s, 6), "gflops": round((sf + sb) / t_s / 1e9, 3),
+                             "runs": "1 warm-up + median of 3"}
+        gcfg = si.CAUSAL_WORKLOADS[GQA]
+        gh4 = si.causal_inputs(gcfg["B"], gcfg["Hq"], gcfg["Hkv"], gcfg["T"], gcfg["D"], gcfg["seed"],
+                               with_do=False)
+        t = time.perf_counter()
+        orc.causal_fwd(gh4["q"], gh4["k"], gh4["v"])
+        t4 = time.perf_counter() - t
+        beside[GQA] = {"fwd_s": round(t4, 3), "gflops": round(g_flops / t4 / 1e9, 3), "runs": "1 run",
+                       "gpu_speedup": round(t4 / (g_ms * 1e-3), 1)}
+        t5 = med3(lambda: orc.paged_decode(dh["q"], dh["k_pool"], dh["v_pool"], dh["block_table"],
+                                           dh["context_lens"]))
+        beside[DECODE] = {"s": round(t5, 4), "gbps": round(dbytes / t5 / 1e9, 3), "runs": "1 warm-up + median of 3",
+                          "gpu_speedup": round(t5 / dec_avg_s, 1)}
+        line["cpu_oracle_beside"] = beside
     print(json.dumps(line), flush=True)
 
 
