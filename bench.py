@@ -105,10 +105,11 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="only fill, sum and copy a buffer of this many MiB (plain kernels of known "
                          "traffic, to scale hardware byte counters) and exit")
-    ap.add_argument("--only", choices=["all", "bwd", "gqa", "decode"], default="all",
+    ap.add_argument("--only", choices=["all", "bwd", "gqa", "decode", "prefill"], default="all",
                     help="'bwd': run only the timed steps of forward + backward; 'gqa': only the 8192-token "
                          "grouped-query forward and backward, --gqa-iters times each; 'decode': only --steps "
-                         "decode calls on the pool replicas (for counter passes)")
+                         "decode calls on the pool replicas; 'prefill': only --steps prefill calls (for counter "
+                         "passes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the library runs on one GPU (got --gpus {args.gpus}); "
@@ -152,6 +153,18 @@ def main():
                                  workspace=gws, stream=stream)
         torch.cuda.synchronize()
         print(json.dumps({"only": "gqa", "iters": args.gqa_iters}), flush=True)
+        return
+
+    if args.only == "prefill":
+        ph = si.prefill_workload(PREFILL)
+        pdev = {k: ph[k].to(dev) for k in ("q", "k_pool", "v_pool", "block_table", "context_lens", "token_start")}
+        po = torch.empty_like(pdev["q"])
+        plse = torch.empty((ph["N"], si.PREFILL_WORKLOADS[PREFILL]["Hq"]), device=dev)
+        for _ in range(args.steps):
+            attn.attn_paged_prefill(pdev["q"], pdev["k_pool"], pdev["v_pool"], pdev["block_table"],
+                                    pdev["context_lens"], pdev["token_start"], o=po, lse=plse, stream=stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "prefill", "calls": args.steps}), flush=True)
         return
 
     # ---- inputs and outputs, resident before timing ----

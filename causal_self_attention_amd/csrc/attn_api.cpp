@@ -74,11 +74,12 @@ attn_status check_ptr(const void* p, const char* name, size_t align) {
 
 const int64_t kMaxElems = (int64_t)1 << 31;  // per-head T*D and index arithmetic limit
 
-// Launch grids: one forward work-group per 64-row block and head; the backward's
+// Launch grids: one forward work-group per 64-row block and head (plus fewer than 8
+// groups of Hq/Hkv padding work-groups for the XCD-grouped order); the backward's
 // preprocess takes D/4 threads per row.  Both stay far below 2^31 work-groups here
 // (B*Hq*T*D < 2^40 floats is 4 TB, beyond any device memory).
 bool causal_grid_fits(int64_t B, int64_t Hq, int64_t T, int64_t D) {
-    return (T + 63) / 64 * (B * Hq) < kMaxElems && B * Hq * T * D < ((int64_t)1 << 40);
+    return (T + 63) / 64 * (B * Hq) + 8 * Hq < kMaxElems && B * Hq * T * D < ((int64_t)1 << 40);
 }
 
 // Shape checks shared by the two causal calls.
@@ -572,7 +573,7 @@ attn_status attn_paged_prefill(const float* q, const float* k_pool, const float*
             return fail(ATTN_INVALID_ARGUMENT, "Hq % Hkv != 0: query heads cannot be grouped over the key/value heads");
         if (!std::isfinite(scale)) return fail(ATTN_INVALID_ARGUMENT, "scale is not finite");
         if (page_size * max_pages_per_seq >= kMaxElems || S * max_pages_per_seq >= kMaxElems ||
-            N * Hq * D >= kMaxElems || (N / 64 + S) * Hq >= kMaxElems ||
+            N * Hq * D >= kMaxElems || (N / 64 + S + 8) * Hq >= kMaxElems ||
             num_pages * Hkv * page_size * D >= ((int64_t)1 << 40))
             return fail(ATTN_INVALID_ARGUMENT, "attn_paged_prefill: sizes too large");
         if (!attn::causal_head_dim_supported(D) || (page_size != 16 && page_size != 32 && page_size != 64))

@@ -110,12 +110,16 @@ __global__ __launch_bounds__(256 * KQ) void attn_fwd_kernel(
     const int li = lane & 15;
     const int g = lane >> 4;
 
-    const int rank = snake_rank(blockIdx.x, nqb * nbh, ncu);
+    // the query heads of a KV head on one XCD, then heavy and light blocks paired on a CU
+    const int G = Hq / Hkv;
+    const int item = xcd_grouped_item(blockIdx.x, G, nqb * nbh / G);
+    if (item < 0) return;  // uniform: a padding work-group, before any barrier
+    const int rank = snake_rank(item, nqb * nbh, ncu);
     const int qb = nqb - 1 - rank / nbh;  // rank 0 = the longest causal prefix
     const int bh = rank % nbh;
     const int b = bh / Hq;
     const int h = bh % Hq;
-    const int hk = h / (Hq / Hkv);
+    const int hk = h / G;
     const float* Qh = Q + ((size_t)b * Hq + h) * (size_t)T * D;
     const float* Kh = K + ((size_t)b * Hkv + hk) * (size_t)T * D;
     const float* Vh = V + ((size_t)b * Hkv + hk) * (size_t)T * D;
@@ -362,7 +366,9 @@ static hipError_t launch_fwd_d(const FwdArgs& a, hipStream_t stream) {
     // work-group to whichever CU frees up first)
     const int n = nqb * nbh;
     const int ncu = KQ == 2 && n <= 2 * a.cu_count ? a.cu_count : n;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, KQ>), dim3((unsigned)(nqb * nbh)), dim3(Tr::NT), 0, stream, a.q, a.k,
+    const int64_t G = a.Hq / a.Hkv;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, KQ>), dim3((unsigned)xcd_grouped_grid(G, (int64_t)n / G)), dim3(Tr::NT), 0,
+                       stream, a.q, a.k,
                        a.v, a.o, a.lse, (int)a.Hq, (int)a.Hkv, (int)a.T, nqb, nbh, ncu, c2);
     return hipGetLastError();
 }

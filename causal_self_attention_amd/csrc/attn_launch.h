@@ -89,6 +89,27 @@ __device__ __forceinline__ int snake_rank(int id, int n, int ncu) {
     return (round & 1) ? base + (m - 1 - (id - base)) : id;
 }
 
+// XCD-aware work order.  Work-group x runs on XCD x % kXcds (round-robin dispatch over
+// the 8 XCDs, each with its own L2).  Work items come in groups of G consecutive
+// indices that read the same K/V (the query heads of one KV head); this maps work-group x
+// to an item index so that the G items of a group go to work-groups on one XCD in
+// consecutive dispatch slots -- x = (grp % 8) + 8 * ((grp / 8) * G + i) for item
+// grp * G + i -- and their K/V tiles are fetched into that XCD's L2 once.  The order of
+// the groups is kept to within 8 groups, and x + 8 G m maps to the item 8 G m further on
+// (so a pairing of work-groups x and x + ncu with ncu a multiple of 8 G is preserved).
+// Returns -1 for the padding work-groups past the last group (the grid is rounded up to
+// whole sets of 8 groups).  G == 1 is the identity.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_grouped_item(int x, int G, int ngroups) {
+    if (G == 1) return x < ngroups ? x : -1;
+    const int slot = x / kXcds;
+    const int grp = (slot / G) * kXcds + x % kXcds;
+    return grp < ngroups ? grp * G + slot % G : -1;
+}
+inline int64_t xcd_grouped_grid(int64_t G, int64_t ngroups) {
+    return G == 1 ? ngroups : (ngroups + kXcds - 1) / kXcds * kXcds * G;
+}
+
 // Kernels exist for these head widths / page sizes.
 bool causal_head_dim_supported(int64_t D);
 bool decode_shape_supported(int64_t D, int64_t page_size, int64_t group);

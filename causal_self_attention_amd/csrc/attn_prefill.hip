@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kp, const float* __restrict__ Vp,
     const int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, const int32_t* __restrict__ TS,
     float* __restrict__ O, float* __restrict__ LSE, int S, int N, int Hq, int Hkv, int PS, int max_pages,
-    int num_pages, float c2 /* scale * log2(e) */) {
+    int num_pages, int ngroups, float c2 /* scale * log2(e) */) {
     using Tr = PrefillTraits<D>;
     __shared__ __attribute__((aligned(16))) float smem[Tr::SMEM_FLOATS];
     __shared__ int sel[2];  // this work-group's sequence and query block (-1: none)
@@ -116,8 +116,11 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const int kh = w >> 2;  // key half: sub-tiles 2kh, 2kh+1 of every tile
     const int li = lane & 15;
     const int g = lane >> 4;
-    const int item = blockIdx.x / Hq;
-    const int h = blockIdx.x % Hq;
+    // the query heads of a KV head on one XCD (their K/V pages fetched into its L2 once)
+    const int wi = xcd_grouped_item(blockIdx.x, Hq / Hkv, ngroups);
+    if (wi < 0) return;  // uniform: a padding work-group, before any barrier
+    const int item = wi / Hq;
+    const int h = wi % Hq;
 
     // Which (sequence, block) is item number `item`.  Items run heaviest block first
     // over the whole batch (most key tiles; ties by sequence, then block), so the
@@ -450,10 +453,11 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
     using Tr = PrefillTraits<D>;
     // at most floor(N / 64) + S query blocks over the batch, whatever the split
     const int64_t items = a.N / Tr::BM + a.S;
-    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3((unsigned)(items * a.Hq)), dim3(Tr::NT), 0, stream, a.q,
-                       a.k_pool, a.v_pool, a.block_table, a.context_lens, a.token_start, a.o, a.lse, (int)a.S,
+    const int64_t G = a.Hq / a.Hkv, ngroups = items * a.Hkv;  // (item, KV head) groups of G query heads
+    hipLaunchKernelGGL(attn_prefill_kernel<D>, dim3((unsigned)xcd_grouped_grid(G, ngroups)), dim3(Tr::NT), 0, stream,
+                       a.q, a.k_pool, a.v_pool, a.block_table, a.context_lens, a.token_start, a.o, a.lse, (int)a.S,
                        (int)a.N, (int)a.Hq, (int)a.Hkv, (int)a.page_size, (int)a.max_pages, (int)a.num_pages,
-                       a.scale * kLog2e);
+                       (int)ngroups, a.scale * kLog2e);
     return hipGetLastError();
 }
 
