@@ -11,7 +11,9 @@ Printed: one JSON line.  `value` is the causal forward+backward rate in
 algorithmic TFLOP/s (14*d per unmasked query-key pair: QK^T and PV forward;
 QK^T recompute, dV, dP, dK, dQ backward) over the event time from before the
 forward to after the backward (the two calls issued back to back); separate
-breakdown steps with an event between the calls give the per-call times.  The
+breakdown steps with an event between the calls give the per-call times (means,
+medians and minima; `frac_by_medians` is the fraction from median(fwd) +
+median(bwd)).  The
 decode rate is the algorithmic HBM bytes per call over the average time of
 back-to-back decode calls between two events (the step's decode call, event to
 event, is reported beside it); `decode_sweep` adds the same shape with one
@@ -490,6 +492,11 @@ def main():
             "fwd_bwd_tflops": round(value, 3), "frac_of_fp32_mfma_peak": round(value / PEAK_FP32_MFMA_TFLOPS, 4),
             "fwd_us_median": round(statistics.median(t_fwd) * 1e3, 2),
             "bwd_us_median": round(statistics.median(t_bwd) * 1e3, 2),
+            "us_min": round(min(t_fb) * 1e3, 2), "fwd_us_min": round(min(t_fwd) * 1e3, 2),
+            "bwd_us_min": round(min(t_bwd) * 1e3, 2),
+            # the same fraction from median(fwd) + median(bwd) of the breakdown steps
+            "frac_by_medians": round((fwd_flops + bwd_flops) / ((statistics.median(t_fwd) + statistics.median(t_bwd))
+                                                                * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
         },
         "decode": {
             "us": round(dec_avg_s * 1e6, 2), "calls_back_to_back": nd,
