@@ -791,7 +791,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(
     const float* __restrict__ Po, const float* __restrict__ Pm, const float* __restrict__ Pl,
-    const int32_t* __restrict__ Meta, float* __restrict__ O, float* __restrict__ LSE, int S, int Hq, int nslots) {
+    const int32_t* __restrict__ Meta, float* __restrict__ O, float* __restrict__ LSE, int Hq, int nslots) {
     constexpr int LPR = D / 4;     // lanes per partial row
     constexpr int RPI = 64 / LPR;  // rows per load instruction
     constexpr int NLD = 64 / RPI;  // load instructions per pass of 64 rows
@@ -1049,7 +1049,7 @@ static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_decode_combine_kernel<D>, dim3((unsigned)(a.S * a.Hq)), dim3(64), 0, stream, Po, Pm, Pl,
-                       Meta, a.o, a.lse, (int)a.S, (int)a.Hq, (int)slots);
+                       Meta, a.o, a.lse, (int)a.Hq, (int)slots);
     return hipGetLastError();
 }
 
