@@ -141,6 +141,23 @@ def _dev(t, name, dtype=torch.float32):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _given(t, shape, name):
+    """A caller-provided output must have exactly the shape the call writes: the C ABI
+    takes only its pointer and writes as many elements as the inputs' sizes imply."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _causal_shapes(q, k, v):
+    """B, Hq, Hkv, T, D of q [B,Hq,T,D] and k, v [B,Hkv,T,D]."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError(f"expected q [B,Hq,T,D], k/v [B,Hkv,T,D]; got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, Hq, T, D = q.shape
+    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return B, Hq, k.shape[1], T, D
+
+
 def _same_device(*ts):
     dev = ts[0].device
     for t in ts[1:]:
@@ -168,12 +185,9 @@ def attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages_per_se
 def attn_causal_fwd(q, k, v, scale=None, o=None, lse=None, stream=None):
     """O [B,Hq,T,D] and LSE [B,Hq,T] of causal attention (async on the stream)."""
     dev = _same_device(q, k, v)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError(f"expected q [B,Hq,T,D], k/v [B,Hkv,T,D]; got {tuple(q.shape)}, {tuple(k.shape)}")
-    B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape[0] != B or k.shape[2] != T or k.shape[3] != D:
-        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    B, Hq, Hkv, T, D = _causal_shapes(q, k, v)
+    _given(o, q.shape, "o")
+    _given(lse, (B, Hq, T), "lse")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     with _alloc_on(stream, o, lse):
         if o is None:
@@ -189,10 +203,11 @@ def attn_causal_bwd(q, k, v, o, lse, dout, scale=None, dq=None, dk=None, dv=None
                     stream=None):
     """(dQ, dK, dV) of the loss sum(dout * O) (async on the stream)."""
     dev = _same_device(q, k, v, o, lse, dout)
-    B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
-    if v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, T):
+    B, Hq, Hkv, T, D = _causal_shapes(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape or lse.shape != (B, Hq, T):
         raise ValueError("shape mismatch among q, k, v, o, lse, dout")
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _given(t, ref.shape, name)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_causal_bwd_workspace_bytes(B, Hq, Hkv, T, D)
     with _alloc_on(stream, dq, dk, dv, workspace):
@@ -222,6 +237,8 @@ def attn_paged_decode(q, k_pool, v_pool, block_table, context_lens, scale=None, 
     if Dk != D or block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("shape mismatch among q, pools, block_table, context_lens")
     max_pages = block_table.shape[1]
+    _given(o, q.shape, "o")
+    _given(lse, (S, Hq), "lse")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_paged_decode_workspace_bytes(S, Hq, Hkv, D, page_size, max_pages)
     with _alloc_on(stream, o, lse if with_lse else o, workspace):
@@ -268,8 +285,8 @@ class PreparedPagedDecode:
                 lse = torch.empty((S, Hq), device=dev, dtype=torch.float32)
             if workspace is None:
                 workspace = torch.empty((max(need, 256) // 4,), device=dev, dtype=torch.float32)
-        if o.shape != q.shape or (lse is not None and lse.shape != (S, Hq)):
-            raise ValueError("o must be [S,Hq,D] and lse [S,Hq]")
+        _given(o, q.shape, "o")
+        _given(lse, (S, Hq), "lse")
         lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
         self.o, self.lse = o, lse
         self._keep = (q, k_pool, v_pool, block_table, context_lens, workspace)
@@ -300,8 +317,8 @@ def attn_paged_decode_noalloc(q, k_pool, v_pool, block_table, context_lens, o, l
     num_pages, Hkv, page_size, Dk = k_pool.shape
     if Dk != D or block_table.dim() != 2 or block_table.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("shape mismatch among q, pools, block_table, context_lens")
-    if o.shape != q.shape or (lse is not None and lse.shape != (S, Hq)):
-        raise ValueError("o must be [S,Hq,D] and lse [S,Hq]")
+    _given(o, q.shape, "o")
+    _given(lse, (S, Hq), "lse")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     lse_p = _dev(lse, "lse") if lse is not None else ctypes.c_void_p(0)
     _check(lib().attn_paged_decode_noalloc(_dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
@@ -319,10 +336,10 @@ def attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D) -> int:
 def attn_materialized_fwd(q, k, v, scale=None, o=None, lse=None, p=None, stream=None):
     """O [B,Hq,T,D], LSE [B,Hq,T] and the probabilities P [B,Hq,T,T] (async)."""
     dev = _same_device(q, k, v)
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
-        raise ValueError(f"expected q [B,Hq,T,D], k/v [B,Hkv,T,D]; got {tuple(q.shape)}, {tuple(k.shape)}")
-    B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, T, D = _causal_shapes(q, k, v)
+    _given(o, q.shape, "o")
+    _given(lse, (B, Hq, T), "lse")
+    _given(p, (B, Hq, T, T), "p")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     with _alloc_on(stream, o, lse, p):
         if o is None:
@@ -340,10 +357,13 @@ def attn_materialized_bwd(q, k, v, o, p, dout, dp=None, scale=None, dq=None, dk=
                           stream=None):
     """(dQ, dK, dV) of sum(dout * O) + sum(dp * P) using the stored probabilities p (async)."""
     dev = _same_device(q, k, v, o, p, dout)
-    B, Hq, T, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, T, D = _causal_shapes(q, k, v)
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
     if p.shape != (B, Hq, T, T) or (dp is not None and dp.shape != p.shape):
         raise ValueError("p (and dp) must be [B, Hq, T, T]")
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _given(t, ref.shape, name)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     need = attn_materialized_bwd_workspace_bytes(B, Hq, Hkv, T, D)
     with _alloc_on(stream, dq, dk, dv, workspace):
@@ -448,6 +468,8 @@ def attn_paged_prefill(q, k_pool, v_pool, block_table, context_lens, token_start
     S = block_table.shape[0]
     if Dk != D or block_table.dim() != 2 or context_lens.shape != (S,) or token_start.shape != (S + 1,):
         raise ValueError("shape mismatch among q, pools, block_table, context_lens, token_start")
+    _given(o, q.shape, "o")
+    _given(lse, (N, Hq), "lse")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     with _alloc_on(stream, o, lse if with_lse else o):
         if o is None:
