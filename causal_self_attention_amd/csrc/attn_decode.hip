@@ -258,6 +258,13 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // out-of-bounds read.
 constexpr int kDecodeScanChunks = 16;  // largest NCH: up to 1024 sequences on the split path
 
+// The partition charges each sequence's start this many 16-position groups of work (a
+// share that covers a sequence boundary writes one more partial, the merge of its
+// position lanes): the list cut into equal shares is, per sequence, kDecodeSeqCost
+// charge units followed by the sequence's groups, so a share holding a boundary gets
+// that many groups fewer.
+constexpr int kDecodeSeqCost = 2;
+
 template <int NCH>
 struct DecodePartition {
     int incl[NCH];  // P_{s+1} at lane s % 64 of chunk s / 64
@@ -265,6 +272,7 @@ struct DecodePartition {
     int base[NCH];  // first partial slot of sequence s (exclusive prefix sum of the counts)
     int cnt[NCH];   // partials of sequence s: the work-groups its groups fall to
     int total;      // P_S
+    int vtotal;     // total + kDecodeSeqCost * S: the length of the charged list
     int nact;       // active work-groups: min(nwg, total)
 
     // Two steps, so that other loads can be issued between them: load() issues the
@@ -284,6 +292,7 @@ struct DecodePartition {
             carry = __builtin_amdgcn_readlane(incl[c], 63);
         }
         total = wave_uniform(carry);
+        vtotal = total + kDecodeSeqCost * S;
         nact = min(nwg, total);
         // partial slots: sequence s owns cnt_s = owner(P_{s+1} - 1) - owner(P_s) + 1 of them
         // (0 when empty), consecutive from base_s; there are at most nact + S - 1 in all
@@ -291,7 +300,7 @@ struct DecodePartition {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
             const int pe = incl[c], ps = pe - (len[c] + 15) / 16;
-            cnt[c] = pe > ps ? owner(pe - 1) - owner(ps) + 1 : 0;
+            cnt[c] = pe > ps ? owner(pe - 1, 64 * c + lane) - owner(ps, 64 * c + lane) + 1 : 0;
             base[c] = carry2 + wave_incl_scan(cnt[c]) - cnt[c];
             carry2 = __builtin_amdgcn_readlane(base[c] + cnt[c], 63);
         }
@@ -315,11 +324,27 @@ struct DecodePartition {
     __device__ __forceinline__ int length(int s) const { return at(len, s); }
     __device__ __forceinline__ int first_slot(int s) const { return at(base, s); }
     __device__ __forceinline__ int slots(int s) const { return at(cnt, s); }
-    // the work-group owning group u (total > 0): work-group w takes groups [w N / n, (w+1) N / n)
-    __device__ __forceinline__ int owner(int u) const {
-        if ((int64_t)total * nact < ((int64_t)1 << 31))  // wave-uniform: 32-bit when it cannot overflow
-            return (int)(((uint32_t)(u + 1) * (uint32_t)nact - 1u) / (uint32_t)total);
-        return (int)((((int64_t)u + 1) * nact - 1) / total);
+    // Group u of sequence s sits at u + kDecodeSeqCost (s + 1) in the charged list, and
+    // work-group w takes places [w V / n, (w+1) V / n) of it (V = vtotal): the work-group
+    // owning group u of sequence s (total > 0)
+    __device__ __forceinline__ int owner(int u, int s) const {
+        const int v = u + kDecodeSeqCost * (s + 1);
+        if ((int64_t)vtotal * nact < ((int64_t)1 << 31))  // wave-uniform: 32-bit when it cannot overflow
+            return (int)(((uint32_t)(v + 1) * (uint32_t)nact - 1u) / (uint32_t)vtotal);
+        return (int)((((int64_t)v + 1) * nact - 1) / vtotal);
+    }
+    // the first group at place v of the charged list or later (total if none): work-group w
+    // holds groups [first_group(w V / n), first_group((w+1) V / n)), possibly none
+    __device__ __forceinline__ int first_group(int v, int S) const {
+        const int lane = threadIdx.x & 63;
+        int n = 0;  // sequences whose charged span ends at or before v
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int s = 64 * c + lane;
+            n += __popcll(__ballot(s < S && incl[c] + kDecodeSeqCost * (s + 1) <= v));
+        }
+        if (n >= S) return total;
+        return max(start(n), v - kDecodeSeqCost * (n + 1));
     }
     // Writes each sequence's (first group, length, first slot, slot count) to part[s],
     // so that a wave can drop the per-lane arrays and read one record per sequence.
@@ -341,9 +366,11 @@ struct DecodePartition {
 
 // Balanced split path (fewer (sequence, KV head) pairs than CUs).  The 16-position
 // groups of all sequences form one list, sequence after sequence (N groups in all);
-// work-group w of n = min(nwg, N) takes groups [w N / n, (w+1) N / n), so every
-// work-group streams the same number of K/V bytes to within one group, whatever the
-// mix of context lengths.  A range may start or end inside a sequence and may cover
+// work-group w of n = min(nwg, N) takes places [w V / n, (w+1) V / n) of the list with
+// kDecodeSeqCost charge units before each sequence's groups (V = N + kDecodeSeqCost S),
+// so every work-group streams the same number of K/V bytes to within one group, less
+// one group's worth for each sequence start it holds, whatever the mix of context
+// lengths.  A range may start or end inside a sequence and may cover
 // several: for each sequence it touches the work-group writes one partial (m, l, o) of
 // every query head of its KV heads, into slot base_s + (w - owner(first group of s)):
 // a sequence's partials are consecutive and there are at most n + S - 1 in all.  The
@@ -365,8 +392,9 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     pt.scan(S, PS * max_pages, nwg);
     const int wg = blockIdx.x;
     if (wg >= pt.nact) return;
-    const int u_lo = wave_uniform((int)(((int64_t)wg * pt.total) / pt.nact));
-    const int u_hi = wave_uniform((int)(((int64_t)(wg + 1) * pt.total) / pt.nact));
+    const int u_lo = wave_uniform(pt.first_group((int)(((int64_t)wg * pt.vtotal) / pt.nact), S));
+    const int u_hi = wave_uniform(pt.first_group((int)(((int64_t)(wg + 1) * pt.vtotal) / pt.nact), S));
+    if (u_lo >= u_hi) return;  // a share of charge units only
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
@@ -393,7 +421,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 
         // partial: head h = 4g + r lives in lanes (g, *), register r; head li's l in lanes (*, li)
         const float lt = rows4_sum(l);
-        const int k = wg - pt.owner(ps);  // this partial's place among the sequence's
+        const int k = wg - pt.owner(ps, s);  // this partial's place among the sequence's
         const int first = wave_uniform(pt.first_slot(s));
         const int nslots = wave_uniform(pt.slots(s));  // read with the whole wave active
         if (k == 0 && blockIdx.y == 0 && w == 0 && lane == 0) {  // one writer per sequence
@@ -570,8 +598,9 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
     pt.scan(S, PS * max_pages, nwg);
     const int wg = blockIdx.x;
     if (wg >= pt.nact) return;
-    const int u_lo = wave_uniform((int)(((int64_t)wg * pt.total) / pt.nact));
-    const int u_hi = wave_uniform((int)(((int64_t)(wg + 1) * pt.total) / pt.nact));
+    const int u_lo = wave_uniform(pt.first_group((int)(((int64_t)wg * pt.vtotal) / pt.nact), S));
+    const int u_hi = wave_uniform(pt.first_group((int)(((int64_t)(wg + 1) * pt.vtotal) / pt.nact), S));
+    if (u_lo >= u_hi) return;  // a share of charge units only
     int s_walk = wave_uniform(pt.ended_by(u_lo, S));  // the sequence of group u_lo
     pt.store(part, S);
     const int lane = threadIdx.x & 63;
@@ -623,7 +652,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_valu_kernel(
         int base = 0, dup = 0;
         scatter_sum_positions<LB, V, V>(val, lane, base, dup);
         const int4 info = part[s];
-        const int k = wg - pt.owner(wave_uniform(info.x));  // this partial's place among the sequence's
+        const int k = wg - pt.owner(wave_uniform(info.x), s);  // this partial's place among the sequence's
         const int first = wave_uniform(info.z);
         const int nslots = wave_uniform(info.w);
         if (k == 0 && blockIdx.y == 0 && w == 0 && lane == 0) {  // one writer per sequence
