@@ -86,14 +86,19 @@ def test_prefill_ragged(dev, orc, Hq, Hkv, D, ps, cached, new):
     assert torch.equal(o, o3) and torch.equal(lse, lse3)
 
 
-def test_prefill_workload_sampled(dev, orc):
+def test_prefill_workload(dev, orc):
     """The 8-sequence workload (4172 new tokens, contexts up to 2737 positions) in the
-    configuration the bench times; rows sampled for the oracle, each checked as a
-    one-token prefill at its own position."""
+    configuration the bench times: whole O and LSE against the oracle's batched prefill,
+    and sampled rows against a second route, each row as a one-token prefill at its own
+    position."""
     name = next(iter(si.PREFILL_WORKLOADS))
     announce(f"prefill workload {name}")
     d = si.prefill_workload(name)
     o, lse = _prefill(d, dev)
+    wo, wlse = orc.paged_prefill(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["context_lens"],
+                                 d["token_start"])
+    assert rel_err(o, wo) <= TOL_O, ("O", rel_err(o, wo))
+    assert rel_err(lse, wlse) <= TOL_LSE, ("LSE", rel_err(lse, wlse))
     ts, ctx = d["token_start"].tolist(), d["context_lens"].tolist()
     rows, seqs, pos = [], [], []
     for s in range(len(ctx)):
