@@ -13,7 +13,8 @@ QK^T recompute, dV, dP, dK, dQ backward) over the event time from before the
 forward to after the backward (the two calls issued back to back); separate
 breakdown steps with an event between the calls give the per-call times (means,
 medians and minima; `frac_by_medians` is the fraction from median(fwd) +
-median(bwd)).  The
+median(bwd)); `back_to_back_us` times the same pairs issued back to back between two
+events, with no marker between the calls, as a training loop issues them.  The
 decode rate is the algorithmic HBM bytes per call over the average time of
 back-to-back decode calls between two events (the step's decode call, event to
 event, is reported beside it); `decode_sweep` adds the same shape with one
@@ -250,6 +251,18 @@ def main():
     t_fwd = [e[0].elapsed_time(e[1]) for e in bev]
     t_bwd = [e[1].elapsed_time(e[2]) for e in bev]
     sum_fwd, sum_bwd = sum(t_fwd), sum(t_bwd)
+
+    # the same pass back to back: K forward + backward pairs between two events, with no
+    # marker between the calls (as a training loop issues them); reported beside `value`
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(K):
+        attn.attn_causal_fwd(x["q"], x["k"], x["v"], o=o, lse=lse, stream=stream)
+        attn.attn_causal_bwd(x["q"], x["k"], x["v"], o, lse, x["dout"], dq=dq, dk=dk, dv=dv, workspace=ws,
+                             stream=stream)
+    b1.record(stream)
+    torch.cuda.synchronize()
+    fb_b2b_s = b0.elapsed_time(b1) / K * 1e-3
 
     # headline: fwd+bwd algorithmic TFLOP/s over the event time of the two calls
     value = (fwd_flops + bwd_flops) * K / (sum(t_fb) * 1e-3) / 1e12
@@ -494,6 +507,8 @@ def main():
             "bwd_us_median": round(statistics.median(t_bwd) * 1e3, 2),
             "us_min": round(min(t_fb) * 1e3, 2), "fwd_us_min": round(min(t_fwd) * 1e3, 2),
             "bwd_us_min": round(min(t_bwd) * 1e3, 2),
+            "back_to_back_us": round(fb_b2b_s * 1e6, 2),
+            "back_to_back_frac": round((fwd_flops + bwd_flops) / fb_b2b_s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
             # the same fraction from median(fwd) + median(bwd) of the breakdown steps
             "frac_by_medians": round((fwd_flops + bwd_flops) / ((statistics.median(t_fwd) + statistics.median(t_bwd))
                                                                 * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
