@@ -218,52 +218,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     constexpr int PER = (Tr::TILE4 + Tr::NT - 1) / Tr::NT;
     f32x4 xq[PER], xo[PER];
     float xl = INFINITY, xd = 0.f;
+    float kf[Tr::KSTEPS], vf[Tr::KSTEPS];  // K, V fragments of this lane's key
+    f32x4 kt[PER];                         // this thread's rows of the K tile, on their way to LDS
 
-    // One segment per key block that the run touches (at most two; wave-uniform).
-    for (int64_t s = s_begin; s < s_end; ++pi) {
-        const int kb = runs ? kb_at(pi) : kb_fixed;
-        const int64_t kb_first = runs ? start_at(pi) : 0;
+    // The segment of the run that starts at step s0, position p0 of the pair order: its
+    // key block and its steps [j0, j1) within the block (at most two segments per run
+    // with half pairs; wave-uniform).
+    int kb = 0, j0 = 0, j1 = 0;
+    bool whole = false;
+    int64_t seg_end = 0;
+    auto locate = [&](int64_t s0, int p0) {
+        kb = runs ? kb_at(p0) : kb_fixed;
+        const int64_t kb_first = runs ? start_at(p0) : 0;
         const int64_t kb_end = kb_first + (int64_t)G * (nqb - kb);
-        const int64_t seg_end = s_end < kb_end ? s_end : kb_end;
-        const bool whole = (s == kb_first && seg_end == kb_end);  // no other run shares this key block
-        const int j0 = (int)(s - kb_first), j1 = (int)(seg_end - kb_first);
-        s = seg_end;
-        const int nqt = nqb - kb;
-        const int kv0 = kb * Tr::BN;
-        const int keyw = kv0 + 16 * w + li;  // this lane's key (column of the S / dP tiles)
+        seg_end = s_end < kb_end ? s_end : kb_end;
+        whole = (s0 == kb_first && seg_end == kb_end);  // no other run shares this key block
+        j0 = (int)(s0 - kb_first);
+        j1 = (int)(seg_end - kb_first);
+    };
 
-        __syncthreads();  // the previous segment's readers of Kt are done
+    // Step j of key block kb is query head hk*G + j / (nqb - kb), query tile kb + j % (nqb - kb).
+    // A step's Q, dO rows and row statistics are loaded into registers during the previous
+    // step's dQ phase (or with the segment's K, V) and written to LDS at the top of the step.
+    auto prefetch = [&](int step) {
+        const int nqt_ = nqb - kb;
+        const int h = hk * G + step / nqt_;
+        const int q0 = (kb + step % nqt_) * Tr::BM;
+        const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            const int row = idx / (D / 4), c4 = idx % (D / 4);
+            const int q = q0 + row;
+            xq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            xo[i] = xq[i];
+            if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && q < T) {
+                xq[i] = *(const f32x4*)(Q + (hoff + q) * D + 4 * c4);
+                xo[i] = *(const f32x4*)(dO + (hoff + q) * D + 4 * c4);
+            }
+        }
+        if (tid < Tr::BM) {
+            const int q = q0 + tid;
+            // a padding row gets LSE = +inf, so its probabilities are exactly 0
+            xl = !MAT && q < T ? LSE[hoff + q] * kLog2e : INFINITY;
+            xd = q < T ? Delta[hoff + q] : 0.f;
+        }
+    };
 
-        // K, V fragments of this lane's key: slot s holds [keyw][frag_dim_b(s, g)]
-        float kf[Tr::KSTEPS], vf[Tr::KSTEPS];
+    // What a segment reads from memory before its first step, issued at once into
+    // registers: this lane's K, V fragments (slot s holds [key][frag_dim_b(s, g)]), its
+    // rows of the K tile and (with_q) the first step's Q, dO rows.  For a run's second
+    // segment the K, V part is issued before the first segment's dK, dV leave, so that
+    // those loads do not queue behind the writes (1-2 % at the 1024- and 8192-token
+    // shapes); the Q, dO rows follow the writes, since holding them across the atomic
+    // flush as well made the compiler spill registers.  The materialized variant, which
+    // holds more state, loads everything after the writes.
+    auto load_segment = [&](bool with_q) {
+        const int keyw_ = kb * Tr::BN + 16 * w + li;
 #pragma unroll
         for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
             const int d0 = 4 * Tr::W * u + Tr::W * g;
             if constexpr (Tr::W == 4) {
-                f32x4 x = !MAT && keyw < T ? *(const f32x4*)(Kh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
-                f32x4 y = keyw < T ? *(const f32x4*)(Vh + (size_t)keyw * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 x = !MAT && keyw_ < T ? *(const f32x4*)(Kh + (size_t)keyw_ * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                f32x4 y = keyw_ < T ? *(const f32x4*)(Vh + (size_t)keyw_ * D + d0) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     kf[4 * u + j] = x[j];
                     vf[4 * u + j] = y[j];
                 }
             } else {
-                f32x2 x = !MAT && keyw < T ? *(const f32x2*)(Kh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
-                f32x2 y = keyw < T ? *(const f32x2*)(Vh + (size_t)keyw * D + d0) : f32x2{0.f, 0.f};
+                f32x2 x = !MAT && keyw_ < T ? *(const f32x2*)(Kh + (size_t)keyw_ * D + d0) : f32x2{0.f, 0.f};
+                f32x2 y = keyw_ < T ? *(const f32x2*)(Vh + (size_t)keyw_ * D + d0) : f32x2{0.f, 0.f};
                 kf[2 * u] = x[0];
                 kf[2 * u + 1] = x[1];
                 vf[2 * u] = y[0];
                 vf[2 * u + 1] = y[1];
             }
         }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            const int row = idx / (D / 4), c4 = idx % (D / 4);
+            const int key = kb * Tr::BN + row;
+            kt[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && key < T)
+                kt[i] = *(const f32x4*)(Kh + (size_t)key * D + 4 * c4);
+        }
+        if (with_q) prefetch(j0);
+    };
+
+    locate(s_begin, pi);
+    load_segment(true);
+    for (;;) {
+        const int kv0 = kb * Tr::BN;
+        const int nqt = nqb - kb;
+        const int keyw = kv0 + 16 * w + li;  // this lane's key (column of the S / dP tiles)
+        const int kbs = kb, js0 = j0, js1 = j1;
+        const bool wholes = whole;
+        const int64_t s_next = seg_end;
+
+        __syncthreads();  // the previous segment's readers of Kt, Qs and dOs are done
+
         // the key block's K tile in LDS, transposed (B operand of dQ = dS K: four
         // consecutive keys of one dim are one vector read)
-        for (int idx = tid; idx < Tr::TILE4; idx += Tr::NT) {
-            const int row = idx / (D / 4), c4 = idx % (D / 4);
-            const int key = kv0 + row;
-            const f32x4 x = key < T ? *(const f32x4*)(Kh + (size_t)key * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) Kt[(4 * c4 + c) * Tr::LDT + row] = x[c];
+        for (int i = 0; i < PER; ++i) {
+            const int idx = tid + Tr::NT * i;
+            if (Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) {
+                const int row = idx / (D / 4), c4 = idx % (D / 4);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) Kt[(4 * c4 + c) * Tr::LDT + row] = kt[i][c];
+            }
         }
 
         // dK, dV accumulators as [key 4g + r][dim NDT*li + dt] (this wave's 16 keys)
@@ -274,37 +339,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
             dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 
-        // Step j of the key block is query head hk*G + j / nqt, query tile kb + j % nqt.
-        // The next step's Q, dO rows and row statistics are loaded into registers
-        // during the current step's dQ phase and written to LDS at the top of the next.
-        auto prefetch = [&](int step) {
+        for (int step = js0; step < js1; ++step) {
             const int h = hk * G + step / nqt;
-            const int q0 = (kb + step % nqt) * Tr::BM;
-            const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                const int idx = tid + Tr::NT * i;
-                const int row = idx / (D / 4), c4 = idx % (D / 4);
-                const int q = q0 + row;
-                xq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-                xo[i] = xq[i];
-                if ((Tr::TILE4 % Tr::NT == 0 || idx < Tr::TILE4) && q < T) {
-                    xq[i] = *(const f32x4*)(Q + (hoff + q) * D + 4 * c4);
-                    xo[i] = *(const f32x4*)(dO + (hoff + q) * D + 4 * c4);
-                }
-            }
-            if (tid < Tr::BM) {
-                const int q = q0 + tid;
-                // a padding row gets LSE = +inf, so its probabilities are exactly 0
-                xl = !MAT && q < T ? LSE[hoff + q] * kLog2e : INFINITY;
-                xd = q < T ? Delta[hoff + q] : 0.f;
-            }
-        };
-        prefetch(j0);
-
-        for (int step = j0; step < j1; ++step) {
-            const int h = hk * G + step / nqt;
-            const int qb = kb + step % nqt;
+            const int qb = kbs + step % nqt;
             const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
             float* dQh = dQ + hoff * D;
             {
@@ -331,7 +368,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 // this wave's keys: their probabilities are zeroed by the causal select below.
                 // Skipping them would put branches around accumulating MFMAs, and the compiler
                 // then copies the accumulators at every join, which costs more than it saves.
-                const bool diag = (qb == kb);
+                const bool diag = (qb == kbs);
 
                 // S = Q K^T and dP = dO V^T : C[query 16qs + 4g + r][key li].  MAT: S is not
                 // formed; sa takes the stored P of this lane's (query, key) entries and dP
@@ -447,7 +484,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                     }
                 }
 
-                if (step + 1 < j1) prefetch(step + 1);  // lands during the dQ phase
+                if (step + 1 < js1) prefetch(step + 1);  // lands during the dQ phase
 
                 // dS -> LDS as [query][key]
 #pragma unroll
@@ -465,14 +502,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 for (int u = 0; u < 4; ++u) {
                     {
                         const f32x4 a = *(const f32x4*)&dSs[(16 * w + li) * Tr::LDS_ + 16 * u + 4 * g];
-                        f32x4 kb[Tr::NDT];
+                        f32x4 kop[Tr::NDT];
 #pragma unroll
                         for (int dt = 0; dt < Tr::NDT; ++dt)
-                            kb[dt] = *(const f32x4*)&Kt[(16 * dt + li) * Tr::LDT + 16 * u + 4 * g];
+                            kop[dt] = *(const f32x4*)&Kt[(16 * dt + li) * Tr::LDT + 16 * u + 4 * g];
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
 #pragma unroll
-                            for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = mfma16x16x4(a[j], kb[dt][j], qa[dt]);
+                            for (int dt = 0; dt < Tr::NDT; ++dt) qa[dt] = mfma16x16x4(a[j], kop[dt][j], qa[dt]);
                     }
                 }
                 if constexpr (Tr::NDT % 4 == 0) {
@@ -511,13 +548,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         }
 
         // dK, dV: lane (g, li) holds keys kv0 + 16w + 4g + r, dims NDT*li .. NDT*li+NDT-1.
-        if (whole || runs > nkb) {
+        const bool more = s_next < s_end;  // another segment follows
+        if (wholes || runs > nkb) {
+            if (more && !MAT) {
+                locate(s_next, pi + 1);
+                load_segment(true);
+            }
             // plain stores: into dK, dV when no other run shares this key block, else
             // (finer runs) into this run's workspace slot after Delta: slot 0 for the
             // run's first segment, 1 for its last.
             float* dKb = dKh + (size_t)kv0 * D;
             float* dVb = dVh + (size_t)kv0 * D;
-            if (!whole) {
+            if (!wholes) {
                 const size_t slot = (size_t)(fine_tag >> 16) * 2 + (pi != (fine_tag & 0xFFFF) ? 1 : 0);
                 float* part = const_cast<float*>(Delta) + ((size_t)nbkv * G * T + 63) / 64 * 64;
                 dKb = part + slot * (2 * Tr::BN * D);
@@ -559,6 +601,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 }
             }
             __syncthreads();
+            if (more && !MAT) {
+                locate(s_next, pi + 1);
+                load_segment(false);
+            }
             for (int idx = tid; idx < Tr::BN * D; idx += Tr::NT) {
                 const int kr = idx / D, d = idx % D;
                 if (kv0 + kr < T) {
@@ -567,6 +613,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
                 }
             }
         }
+        if (!more) break;
+        if constexpr (MAT) {
+            locate(s_next, pi + 1);
+            load_segment(true);
+        } else if (!(wholes || runs > nkb)) {
+            prefetch(j0);
+        }
+        ++pi;
     }
 }
 
