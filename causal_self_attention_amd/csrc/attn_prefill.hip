@@ -21,8 +21,8 @@
 //     page ids of its rows one tile ahead of the rows themselves, so no K/V load
 //     waits on a table read;
 //   * the query rows start at an arbitrary position, so the causal mask is applied
-//     per element on every tile that reaches past a wave's first row, and 16-key
-//     sub-tiles wholly past a wave's last row are skipped;
+//     per element on every tile that reaches past a wave's first row, and the P V
+//     products of 16-key sub-tiles wholly past a wave's last row are skipped;
 //   * the grid enumerates (query block, head) over the ragged batch, heaviest block
 //     (most key tiles) first over the whole batch: each work-group finds its block by
 //     bisection on the number of blocks with at least t tiles (one wave, one lane
@@ -319,27 +319,22 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
         const bool masked = kv0 + Tr::BN - 1 > base + j0 + 16 * rw;  // some key past the wave's first row
 
         // S^T = K Q^T over this wave's key half: st[tt] holds
-        // S^T[key = kv0 + 16(2kh + tt) + 4g + r][token = jr]
+        // S^T[key = kv0 + 16(2kh + tt) + 4g + r][token = jr].  Both sub-tiles are formed,
+        // also one past the wave's last position (masked below, its P V skipped), so that
+        // the two accumulation chains interleave with no branch between them.
         f32x4 st[2];
+        st[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[1] = st[0];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int t = 2 * kh + tt;
-            st[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (t < nsub) {
+        for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
+            float a[2][Tr::W];
 #pragma unroll
-                for (int u = 0; u < Tr::KSTEPS / Tr::W; ++u) {
-                    const float* kp = &Ks[(16 * t + li) * Tr::LDK + 4 * Tr::W * u + Tr::W * g];
-                    if constexpr (Tr::W == 4) {
-                        const f32x4 a = *(const f32x4*)kp;
+            for (int tt = 0; tt < 2; ++tt)
+                pf_lds_vec<Tr::W>(&Ks[(16 * (2 * kh + tt) + li) * Tr::LDK + 4 * Tr::W * u + Tr::W * g], a[tt]);
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) st[tt] = mfma16x16x4(a[jj], qf[4 * u + jj], st[tt]);
-                    } else {
-                        const f32x2 a = *(const f32x2*)kp;
-                        st[tt] = mfma16x16x4(a[0], qf[2 * u], st[tt]);
-                        st[tt] = mfma16x16x4(a[1], qf[2 * u + 1], st[tt]);
-                    }
-                }
-            }
+            for (int jj = 0; jj < Tr::W; ++jj)
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) st[tt] = mfma16x16x4(a[tt][jj], qf[Tr::W * u + jj], st[tt]);
         }
 
         // mask and scale to log2 units; this lane's max over its 8 keys of the tile
