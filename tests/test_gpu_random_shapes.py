@@ -73,10 +73,10 @@ def _materialized_cases(n):
     return out
 
 
-CAUSAL = _causal_cases(48)
-DECODE = _decode_cases(30)
-PREFILL = _prefill_cases(24)
-MATERIALIZED = _materialized_cases(12)
+CAUSAL = _causal_cases(120)
+DECODE = _decode_cases(60)
+PREFILL = _prefill_cases(48)
+MATERIALIZED = _materialized_cases(20)
 
 
 @pytest.fixture(scope="module")
