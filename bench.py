@@ -545,7 +545,7 @@ def main():
         "kv_append": {
             "us_median": round(app_us, 2), "bytes_per_call": app_bytes,
             "gbps": round(app_bytes / (app_us * 1e-6) / 1e9, 2), "calls": n_app,
-            "note": "lease + append of one token for 32 sequences; two small launches, latency bound",
+            "note": "lease + append of one token for 32 sequences; one launch (the lease work-group copies the rows), latency bound",
         },
         "wall_s_timed_region": round(wall, 4),
     }

@@ -232,24 +232,6 @@ __device__ __forceinline__ void decode_load_q(const float* __restrict__ Qd, int 
     for (int u = 0; u < Tr::KSTEPS / Tr::KW; ++u) load_vec<Tr::KW>(qrow + 4 * Tr::KW * u + Tr::KW * g, &qf[Tr::KW * u]);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave on DPP moves (no LDS): shifted
-// adds inside each 16-lane row (a lane whose source is outside its row adds 0), then
-// row 0's total into row 1 and row 2's into row 3 (row_bcast:15), then the total of
-// rows 0-1 into rows 2 and 3 (row_bcast:31).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int dpp_add(int x) {
-    return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
-}
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    x = dpp_add<0x111, 0xF>(x);  // row_shr:1
-    x = dpp_add<0x112, 0xF>(x);  // row_shr:2
-    x = dpp_add<0x114, 0xF>(x);  // row_shr:4
-    x = dpp_add<0x118, 0xF>(x);  // row_shr:8
-    x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
-
 // The split path's partition, computed by every wave on its own from the
 // sequence lengths (no LDS, no barrier): lane l of chunk c stands for sequence
 // s = 64c + l (S <= 64 * NCH) and holds P_{s+1}, the number of 16-position groups

@@ -31,42 +31,82 @@ namespace attn {
 
 constexpr int kScanThreads = 1024;
 
-// Exclusive prefix sum of x over the work-group (kScanThreads threads); the
-// group's total goes to *total.  Uses `buf` (kScanThreads ints of LDS).
+// Exclusive prefix sum of x over the work-group (kScanThreads threads, 16 waves): each
+// wave scans its 64 values on DPP moves, the 16 wave totals go through LDS (`buf`, at
+// least 16 ints), and each thread adds the totals of the waves before its own.  The
+// group's total goes to *total.  Two barriers.
 __device__ __forceinline__ int block_exclusive_scan(int x, int* buf, int* total) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
+    constexpr int NW = kScanThreads / 64;
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(x);
+    if (lane == 63) buf[wv] = incl;
     __syncthreads();
-    for (int off = 1; off < kScanThreads; off <<= 1) {  // Hillis-Steele inclusive scan
-        const int y = tid >= off ? buf[tid - off] : 0;
-        __syncthreads();
-        buf[tid] += y;
-        __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int t = buf[i];
+        before += i < wv ? t : 0;
+        all += t;
     }
-    const int incl = buf[tid];
-    *total = buf[kScanThreads - 1];
+    *total = all;
     __syncthreads();  // buf is reused by the next call
-    return incl - x;
+    return before + incl - x;
 }
 
+// Largest single-token append that the lease work-group also copies itself (float4
+// copies of each of K and V, 4 per thread), saving the second launch; larger batches
+// take one copy work-group per sequence.
+constexpr int kKvFusedCopies = 4 * kScanThreads;
+
+// WRITE (at most kScanThreads sequences, kKvFusedCopies float4 of each of K and V): the
+// same work-group also copies the token's rows.  Everything that does not depend on the
+// lease -- the new rows, the stack height, each sequence's current page -- is loaded at
+// the start, so the call costs two dependent rounds of loads (lengths, then the leased
+// page ids) before the stores.
+template <bool WRITE>
 __global__ __launch_bounds__(kScanThreads) void attn_kv_lease_kernel(
-    int32_t* __restrict__ BT, const int32_t* __restrict__ CTX, const int32_t* __restrict__ FREE,
-    int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int PS, int max_pages) {
-    __shared__ int buf[kScanThreads];
+    int32_t* __restrict__ BT, int32_t* __restrict__ CTX, const int32_t* __restrict__ FREE,
+    int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int PS, int max_pages,
+    const float* __restrict__ Kn, const float* __restrict__ Vn, float* __restrict__ Kp, float* __restrict__ Vp,
+    int Hkv, int D, int num_pages) {
+    constexpr int CPT = WRITE ? kKvFusedCopies / kScanThreads : 1;  // float4 copies per thread
+    __shared__ int buf[kScanThreads / 64];
+    __shared__ int pg[WRITE ? kScanThreads : 1], tl[WRITE ? kScanThreads : 1];
     const int tid = threadIdx.x;
     const int cap = PS * max_pages;
-    // pass 1: how many sequences start a page, and is any sequence full
+    const int d4 = D / 4;
+    const int ncopy = WRITE ? S * Hkv * d4 : 0;
+    f32x4 kx[CPT], vx[CPT];
+    if constexpr (WRITE) {
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int idx = tid + kScanThreads * k;
+            if (idx < ncopy) {
+                kx[k] = *(const f32x4*)(Kn + 4 * (size_t)idx);  // rows [S, Hkv, D]: float4 idx
+                vx[k] = *(const f32x4*)(Vn + 4 * (size_t)idx);
+            }
+        }
+    }
+    const int top = *FCOUNT;
+    // pass 1: how many sequences start a page, and is any sequence full (one scan of
+    // both counts, full ones in the high half: each is at most kScanThreads per chunk)
     int needed = 0, full = 0;
+    int t_own = 1, page_own = 0;  // WRITE: this thread's sequence (s = tid)
     for (int base = 0; base < S; base += kScanThreads) {
         const int s = base + tid;
         const int t = s < S ? CTX[s] : 1;
+        if (WRITE && s < S) {
+            t_own = t;
+            if (t >= 0 && t < cap && t % PS != 0) page_own = BT[(size_t)s * max_pages + t / PS];
+        }
+        const int f = s < S && t >= cap ? 1 : 0;
+        const int nd = s < S && t >= 0 && t < cap && t % PS == 0 ? 1 : 0;
         int tot;
-        block_exclusive_scan(s < S && t >= cap ? 1 : 0, buf, &tot);
-        full += tot;
-        block_exclusive_scan(s < S && t >= 0 && t < cap && t % PS == 0 ? 1 : 0, buf, &tot);
-        needed += tot;
+        block_exclusive_scan((f << 16) | nd, buf, &tot);
+        full += tot >> 16;
+        needed += tot & 0xFFFF;
     }
-    const int top = *FCOUNT;
     if (full > 0 || needed > top) {
         if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
         return;  // uniform
@@ -75,12 +115,40 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_lease_kernel(
     int offset = 0;
     for (int base = 0; base < S; base += kScanThreads) {
         const int s = base + tid;
-        const int t = s < S ? CTX[s] : 1;
+        const int t = s < S ? (WRITE ? t_own : CTX[s]) : 1;
         const bool need = s < S && t >= 0 && t % PS == 0;  // t < cap: no sequence is full here
         int tot;
         const int rank = offset + block_exclusive_scan(need ? 1 : 0, buf, &tot);
-        if (need) BT[(size_t)s * max_pages + t / PS] = FREE[top - 1 - rank];
+        if (need) {
+            const int leased = FREE[top - 1 - rank];
+            BT[(size_t)s * max_pages + t / PS] = leased;
+            page_own = leased;
+        }
         offset += tot;
+    }
+    if constexpr (WRITE) {
+        if (tid < S) {
+            tl[tid] = t_own;
+            pg[tid] = page_own;
+        }
+        __syncthreads();  // pages and positions of every sequence are in LDS
+        // a table entry outside the pool (a broken state) is clamped: wrong data, never an
+        // out-of-bounds write; a negative length (broken) leaves its sequence alone
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const int idx = tid + kScanThreads * k;
+            if (idx < ncopy) {
+                const int s = idx / (Hkv * d4), h = (idx / d4) % Hkv, c = idx % d4;
+                const int t = tl[s];
+                if (t >= 0) {
+                    const int page = min(max(pg[s], 0), num_pages - 1);
+                    const size_t dst = (((size_t)page * Hkv + h) * PS + t % PS) * D + 4 * c;
+                    *(f32x4*)(Kp + dst) = kx[k];
+                    *(f32x4*)(Vp + dst) = vx[k];
+                }
+            }
+        }
+        if (tid < S && t_own >= 0) CTX[tid] = t_own + 1;
     }
     if (tid == 0) {
         *FCOUNT = top - needed;
@@ -115,7 +183,7 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_release_kernel(
     const int32_t* __restrict__ IDS, int n, int32_t* __restrict__ BT, int32_t* __restrict__ CTX,
     int32_t* __restrict__ FREE, int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int PS,
     int max_pages, int num_pages) {
-    __shared__ int buf[kScanThreads];
+    __shared__ int buf[kScanThreads / 64];
     const int tid = threadIdx.x;
     const int cap = PS * max_pages;
     auto pages_of = [&](int i) -> int {  // pages held by sequence IDS[i] (0 for an index out of range)
@@ -172,7 +240,7 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_lease_tokens_kernel(
     int32_t* __restrict__ BT, int32_t* __restrict__ CTX, const int32_t* __restrict__ TS,
     const int32_t* __restrict__ FREE, int32_t* __restrict__ FCOUNT, int32_t* __restrict__ STATUS, int S, int N,
     int PS, int max_pages) {
-    __shared__ int buf[kScanThreads];
+    __shared__ int buf[kScanThreads / 64];
     const int tid = threadIdx.x;
     const int cap = PS * max_pages;
     auto new_pages = [&](int t, int n) { return (t + n + PS - 1) / PS - (t + PS - 1) / PS; };
@@ -259,9 +327,16 @@ hipError_t launch_kv_append_tokens(const KvAppendTokensArgs& a, hipStream_t stre
 }
 
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(attn_kv_lease_kernel, dim3(1), dim3(kScanThreads), 0, stream, a.block_table,
+    if (a.S <= kScanThreads && a.S * a.Hkv * (a.D / 4) <= kKvFusedCopies) {  // lease and copy in one launch
+        hipLaunchKernelGGL(attn_kv_lease_kernel<true>, dim3(1), dim3(kScanThreads), 0, stream, a.block_table,
+                           a.context_lens, a.free_pages, a.free_count, a.status, (int)a.S, (int)a.page_size,
+                           (int)a.max_pages, a.k_new, a.v_new, a.k_pool, a.v_pool, (int)a.Hkv, (int)a.D,
+                           (int)a.num_pages);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(attn_kv_lease_kernel<false>, dim3(1), dim3(kScanThreads), 0, stream, a.block_table,
                        a.context_lens, a.free_pages, a.free_count, a.status, (int)a.S, (int)a.page_size,
-                       (int)a.max_pages);
+                       (int)a.max_pages, nullptr, nullptr, nullptr, nullptr, 0, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_kv_write_kernel, dim3((unsigned)a.S), dim3(256), 0, stream, a.k_new, a.v_new,

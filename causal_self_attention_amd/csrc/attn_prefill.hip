@@ -82,21 +82,6 @@ __device__ __forceinline__ void pf_lds_vec(const float* p, float (&x)[N]) {
     }
 }
 
-// Inclusive prefix sum over a wave on DPP moves (row shifts, then row broadcasts).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ int pf_dpp_add(int x) {
-    return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
-}
-__device__ __forceinline__ int pf_wave_incl_scan(int x) {
-    x = pf_dpp_add<0x111, 0xF>(x);  // row_shr:1
-    x = pf_dpp_add<0x112, 0xF>(x);  // row_shr:2
-    x = pf_dpp_add<0x114, 0xF>(x);  // row_shr:4
-    x = pf_dpp_add<0x118, 0xF>(x);  // row_shr:8
-    x = pf_dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-    x = pf_dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-    return x;
-}
-
 template <int D>
 __global__ __launch_bounds__(512) void attn_prefill_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kp, const float* __restrict__ Vp,
@@ -159,7 +144,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
             int tot = 0;
             for (int c0 = 0; c0 < S; c0 += 64) {
                 const SeqBlocks q = c0 == 0 ? q0 : seq_at(c0 + lane);
-                tot += __builtin_amdgcn_readlane(pf_wave_incl_scan(cnt_ge(q, t)), 63);
+                tot += __builtin_amdgcn_readlane(wave_incl_scan(cnt_ge(q, t)), 63);
             }
             return tot;
         };
@@ -185,7 +170,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(
                 const SeqBlocks q = c0 == 0 ? q0 : seq_at(c0 + lane);
                 const int ge = cnt_ge(q, lo);
                 const int eq = ge - cnt_ge(q, lo + 1);
-                const int incl = carry + pf_wave_incl_scan(eq);
+                const int incl = carry + wave_incl_scan(eq);
                 const uint64_t hit = __ballot(k < incl);
                 if (hit) {
                     const int l = __builtin_ctzll(hit);
