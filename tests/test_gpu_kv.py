@@ -36,7 +36,11 @@ def _assert_same_state(c, m, where):
     assert np.array_equal(c.v_pool.cpu().numpy(), m.v_pool), (where, "v_pool")
 
 
-KV_CASES = [(37, 4, 64, 16, 6, 120), (37, 2, 8, 64, 2, 40), (9, 2, 128, 32, 5, 30), (1500, 1, 16, 16, 2, 2100)]
+# single-token appends up to 1024 sequences and 4096 float4 rows take the one-launch path
+# (lease and copy in one work-group); the second-to-last case is exactly at both limits,
+# the two before it past the row limit, the last past the sequence limit
+KV_CASES = [(37, 4, 64, 16, 6, 120), (37, 2, 8, 64, 2, 40), (9, 2, 128, 32, 5, 30), (100, 8, 64, 16, 3, 250),
+            (40, 16, 128, 16, 4, 150), (1024, 1, 16, 16, 2, 1500), (1500, 1, 16, 16, 2, 2100)]
 
 
 @pytest.mark.parametrize("S,Hkv,D,ps,max_pages,num_pages", KV_CASES)
