@@ -51,8 +51,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 # HBM bytes per attn_causal_bwd launch on the 1024-token workload, from FETCH_SIZE (x2.00)
 # and WRITE_SIZE (x1.00) counter passes; valid only for the kernel source they were taken on.
-BWD_TRAFFIC_BYTES = 164.4e6
-BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "572c0887ce9baa98"
+BWD_TRAFFIC_BYTES = 166.0e6
+BWD_TRAFFIC_SOURCE_SHA256_PREFIX = "4898045732492846"
 CAUSAL = "mha_b4_h8_t1024_d64"
 SMALL = ("mha_b1_h2_t16_d8", "mha_b8_h4_t256_d32")
 GQA = "gqa_b1_hq16_hkv4_t8192_d64"

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
     const float* __restrict__ P, const float* __restrict__ dPx,
     float* __restrict__ dQ, float* __restrict__ dK, float* __restrict__ dV, int Hq, int Hkv, int T,
-    int nkb, int nbkv, int runs, float scale, float c2 /* scale * log2(e) */) {
+    int nkb, int nbkv, int runs, int desc, float scale, float c2 /* scale * log2(e) */) {
     using Tr = BwdTraits<D>;
     __shared__ __attribute__((aligned(16))) float Qs[Tr::BM * Tr::LD];
     __shared__ __attribute__((aligned(16))) float dOs[Tr::BM * Tr::LD];
@@ -237,13 +237,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
         j1 = (int)(seg_end - kb_first);
     };
 
-    // Step j of key block kb is query head hk*G + j / (nqb - kb), query tile kb + j % (nqb - kb).
+    // Step j of key block kb is query head hk*G + j / (nqb - kb) and, with s = j % (nqb - kb),
+    // query tile kb + s, or nqb - 1 - s when desc is set (see the launcher).
+    auto qtile = [&](int kb_, int s) { return desc ? nqb - 1 - s : kb_ + s; };
     // A step's Q, dO rows and row statistics are loaded into registers during the previous
     // step's dQ phase (or with the segment's K, V) and written to LDS at the top of the step.
     auto prefetch = [&](int step) {
         const int nqt_ = nqb - kb;
         const int h = hk * G + step / nqt_;
-        const int q0 = (kb + step % nqt_) * Tr::BM;
+        const int q0 = qtile(kb, step % nqt_) * Tr::BM;
         const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D >= 128 ? 
 
         for (int step = js0; step < js1; ++step) {
             const int h = hk * G + step / nqt;
-            const int qb = kbs + step % nqt;
+            const int qb = qtile(kbs, step % nqt);
             const size_t hoff = ((size_t)b * Hq + h) * (size_t)T;
             float* dQh = dQ + hoff * D;
             {
@@ -690,6 +692,8 @@ static int64_t bwd_fine_runs_max(int64_t B, int64_t Hq, int64_t Hkv, int64_t T) 
 
 static size_t bwd_delta_floats(int64_t B, int64_t Hq, int64_t T) { return (size_t)(B * Hq * T + 63) / 64 * 64; }
 
+constexpr int kBwdDescendingFromTiles = 32;  // 64-key tiles per sequence
+
 template <int D, bool MAT>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
     using Tr = BwdTraits<D>;
@@ -728,9 +732,15 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t stream) {
         if (e != hipSuccess) return e;
     }
     const unsigned grid = runs > 0 ? (unsigned)(runs * nbkv) : (unsigned)n;
+    // Query tiles of a key block in descending order for long sequences: the key blocks of
+    // a head, which run at the same time on one or two XCDs, then read the same Q, dO tiles
+    // at about the same time and find them in that XCD's L2 (measured on one MI355X: 1.5-2 %
+    // faster at B=1, Hq=16, Hkv=4, T=8192, d=64, 0.6-0.7 % at T=2048 and 4096, and no gain
+    // at T=1024, so the order follows the tile count).  dK, dV stay deterministic either way.
+    const int desc = nkb >= kBwdDescendingFromTiles ? 1 : 0;
     hipLaunchKernelGGL((attn_bwd_main_kernel<D, MAT>), dim3(grid), dim3(Tr::NT), 0, stream, a.q, a.k, a.v,
                        a.dout, a.lse, a.delta, a.p, a.dpx, a.dq, a.dk, a.dv, (int)a.Hq, (int)a.Hkv, (int)a.T, nkb,
-                       nbkv, runs, a.scale, a.scale * kLog2e);
+                       nbkv, runs, desc, a.scale, a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess || !part) return e;
     constexpr int chunks = (2 * Tr::BN * D / 4 + 255) / 256;
