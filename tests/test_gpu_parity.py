@@ -193,6 +193,26 @@ def test_backward_fine_schedule(dev, orc, B, Hq, Hkv, T, D):
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,T,D,cut", [(3, 6, 6, 2025, 16, "whole"), (1, 2, 1, 2100, 64, "fine"),
+                                              (2, 8, 4, 4073, 16, "half")])
+def test_backward_descending_query_order(dev, orc, B, Hq, Hkv, T, D, cut):
+    """From 32 key blocks per sequence on, the backward takes a key block's query tiles in
+    descending order: parity under each of the three cuts of the work (the last tile
+    ragged), and bitwise equal dK, dV on a second call."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    assert (T + 63) // 64 >= 32 and _bwd_schedule(cus, B, Hq, Hkv, T, D) == cut
+    announce(f"bwd descending query order ({cut} cut) B={B} Hq={Hq} Hkv={Hkv} T={T} D={D}")
+    host = si.causal_inputs(B, Hq, Hkv, T, D, seed=470 + T + D)
+    x = _to(host, dev)
+    o, lse = _run_fwd(x)
+    dq, dk, dv = _run_bwd(x, o, lse)
+    rdq, rdk, rdv = orc.causal_bwd(host["q"], host["k"], host["v"], host["dout"])
+    for nm, a, b in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+        assert rel_err(a, b) <= TOL_GRAD, (nm, rel_err(a, b))
+    _, dk2, dv2 = _run_bwd(x, o, lse)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
 # ---------------------------------------------------------------------------
 # invariants and closed forms on the GPU outputs
 # ---------------------------------------------------------------------------
