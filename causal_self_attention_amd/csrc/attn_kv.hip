@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_lease_kernel(
     int Hkv, int D, int num_pages) {
     constexpr int CPT = WRITE ? kKvFusedCopies / kScanThreads : 1;  // float4 copies per thread
     __shared__ int buf[kScanThreads / 64];
-    __shared__ int pg[WRITE ? kScanThreads : 1], tl[WRITE ? kScanThreads : 1];
+    __shared__ int pg[WRITE ? kScanThreads : 1], tl[WRITE ? kScanThreads : 1], fr[WRITE ? kScanThreads : 1];
     const int tid = threadIdx.x;
     const int cap = PS * max_pages;
     const int d4 = D / 4;
@@ -89,42 +89,64 @@ __global__ __launch_bounds__(kScanThreads) void attn_kv_lease_kernel(
         }
     }
     const int top = *FCOUNT;
-    // pass 1: how many sequences start a page, and is any sequence full (one scan of
-    // both counts, full ones in the high half: each is at most kScanThreads per chunk)
     int needed = 0, full = 0;
     int t_own = 1, page_own = 0;  // WRITE: this thread's sequence (s = tid)
-    for (int base = 0; base < S; base += kScanThreads) {
-        const int s = base + tid;
+    if constexpr (WRITE) {
+        // One work-group holds the whole batch (S <= kScanThreads): one scan gives both the
+        // counts and each sequence's rank, and the S entries at the top of the free stack
+        // are read as soon as its height is known, beside the lengths' table reads, so
+        // that no global read waits on the scan.
+        const int s = tid;
         const int t = s < S ? CTX[s] : 1;
-        if (WRITE && s < S) {
+        const int fi = top - 1 - tid;  // rank tid would take free_pages[top - 1 - tid]
+        if (tid < S && fi >= 0 && fi < num_pages) fr[tid] = FREE[fi];
+        if (s < S) {
             t_own = t;
             if (t >= 0 && t < cap && t % PS != 0) page_own = BT[(size_t)s * max_pages + t / PS];
         }
         const int f = s < S && t >= cap ? 1 : 0;
         const int nd = s < S && t >= 0 && t < cap && t % PS == 0 ? 1 : 0;
         int tot;
-        block_exclusive_scan((f << 16) | nd, buf, &tot);
-        full += tot >> 16;
-        needed += tot & 0xFFFF;
-    }
-    if (full > 0 || needed > top) {
-        if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
-        return;  // uniform
-    }
-    // pass 2: rank r (index order) takes free_pages[top - 1 - r]
-    int offset = 0;
-    for (int base = 0; base < S; base += kScanThreads) {
-        const int s = base + tid;
-        const int t = s < S ? (WRITE ? t_own : CTX[s]) : 1;
-        const bool need = s < S && t >= 0 && t % PS == 0;  // t < cap: no sequence is full here
-        int tot;
-        const int rank = offset + block_exclusive_scan(need ? 1 : 0, buf, &tot);
-        if (need) {
-            const int leased = FREE[top - 1 - rank];
+        const int ex = block_exclusive_scan((f << 16) | nd, buf, &tot);  // its barriers publish fr
+        full = tot >> 16;
+        needed = tot & 0xFFFF;
+        if (full > 0 || needed > top) {
+            if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
+            return;  // uniform
+        }
+        if (nd) {  // rank = the sequences before it that start a page (none is full here)
+            const int leased = fr[ex & 0xFFFF];
             BT[(size_t)s * max_pages + t / PS] = leased;
             page_own = leased;
         }
-        offset += tot;
+    } else {
+        // pass 1: how many sequences start a page, and is any sequence full (one scan of
+        // both counts, full ones in the high half: each is at most kScanThreads per chunk)
+        for (int base = 0; base < S; base += kScanThreads) {
+            const int s = base + tid;
+            const int t = s < S ? CTX[s] : 1;
+            const int f = s < S && t >= cap ? 1 : 0;
+            const int nd = s < S && t >= 0 && t < cap && t % PS == 0 ? 1 : 0;
+            int tot;
+            block_exclusive_scan((f << 16) | nd, buf, &tot);
+            full += tot >> 16;
+            needed += tot & 0xFFFF;
+        }
+        if (full > 0 || needed > top) {
+            if (tid == 0) *STATUS = full > 0 ? ATTN_KV_SEQUENCE_FULL : ATTN_KV_POOL_EXHAUSTED;
+            return;  // uniform
+        }
+        // pass 2: rank r (index order) takes free_pages[top - 1 - r]
+        int offset = 0;
+        for (int base = 0; base < S; base += kScanThreads) {
+            const int s = base + tid;
+            const int t = s < S ? CTX[s] : 1;
+            const bool need = s < S && t >= 0 && t % PS == 0;  // t < cap: no sequence is full here
+            int tot;
+            const int rank = offset + block_exclusive_scan(need ? 1 : 0, buf, &tot);
+            if (need) BT[(size_t)s * max_pages + t / PS] = FREE[top - 1 - rank];
+            offset += tot;
+        }
     }
     if constexpr (WRITE) {
         if (tid < S) {
